@@ -1,0 +1,32 @@
+"""Compile the CPU oracle (plain C) into oracle/libcfz_oracle.so with gcc.
+
+Strict IEEE semantics: no fast-math and no floating-point contraction, so that
+the only fused multiply-adds are the explicit fmaf calls of the definitions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "cfz_oracle.c")
+LIB = os.path.join(HERE, "libcfz_oracle.so")
+
+CFLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+          "-fno-strict-aliasing", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)
