@@ -1,0 +1,251 @@
+"""Thin ctypes binding over libcfz (``include/cfz.h``): argument marshalling only.
+
+Every step of the codec and of the subspace iteration runs in the HIP kernels
+of ``libcfz.so``; this module converts torch tensors into raw device pointers
+and the current HIP stream, calls the C entry point of the same name, and
+turns a non-OK status into ``CfzError``.  torch supplies device memory and
+streams, nothing else.  There is no fallback: if the library is not built,
+importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcfz.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cfz.h")
+
+CFZ_OK, CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_UNSUPPORTED = 0, 1, 2, 3
+CFZ_ERR_ALIGN, CFZ_ERR_MODE, CFZ_ERR_WORKSPACE, CFZ_ERR_HIP = 4, 5, 6, 7
+CFZ_EF_DELTA, CFZ_EF_LITERAL, CFZ_EF_OFF = 0, 1, 2
+CFZ_SENDER, CFZ_RECEIVER = 0, 1
+MODES = {"delta": CFZ_EF_DELTA, "literal": CFZ_EF_LITERAL, "off": CFZ_EF_OFF}
+
+
+class cfz_desc(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("cols", C.c_int64), ("bits", C.c_int32),
+                ("group", C.c_int32), ("ef_mode", C.c_int32), ("role", C.c_int32)]
+
+
+class cfz_buffers(C.Structure):
+    _fields_ = [("prev_bf16", C.c_void_p), ("base_f32", C.c_void_p), ("err_f32", C.c_void_p)]
+
+
+class CfzError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = _lib.cfz_last_error().decode(errors="replace")
+        name = _lib.cfz_status_string(status).decode()
+        super().__init__(f"{where}: {name} (status {status}): {detail}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libcfz.so is not built ({LIB_PATH}); build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` at the repository root")
+    lib = C.CDLL(LIB_PATH)
+    p, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+    sig = {
+        "cfz_state_create": ([C.POINTER(cfz_desc), C.POINTER(cfz_buffers), p, p, C.POINTER(p)], i32),
+        "cfz_state_resume": ([C.POINTER(cfz_desc), C.POINTER(cfz_buffers), i64, C.POINTER(p)], i32),
+        "cfz_state_destroy": ([p], i32),
+        "cfz_state_steps": ([p], i64),
+        "cfz_codes_bytes": ([C.POINTER(cfz_desc)], sz),
+        "cfz_scales_bytes": ([C.POINTER(cfz_desc)], sz),
+        "cfz_compress": ([p, p, p, p, p], i32),
+        "cfz_decompress": ([p, p, p, p, p], i32),
+        "cfz_lowrank_workspace_bytes": ([i64, i64, i64, i32], sz),
+        "cfz_lowrank": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, sz, p], i32),
+        "cfz_stream_copy": ([p, p, sz, p], i32),
+        "cfz_status_string": ([i32], C.c_char_p),
+        "cfz_last_error": ([], C.c_char_p),
+        "cfz_abi_version": ([], C.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def header_functions():
+    """Names of the functions ``include/cfz.h`` declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cfz_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(status, where):
+    if status != CFZ_OK:
+        raise CfzError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("libcfz takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libcfz takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _bf16_ptr(t):
+    if t is not None and not isinstance(t, int) and t.dtype not in (torch.bfloat16, torch.int16,
+                                                                    torch.uint16):
+        raise TypeError("bf16 data must be a bfloat16 (or 16-bit bit-pattern) tensor")
+    return _ptr(t)
+
+
+# ------------------------------------------------------------------ raw entry points
+
+def cfz_abi_version() -> int:
+    return _lib.cfz_abi_version()
+
+
+def cfz_status_string(status: int) -> str:
+    return _lib.cfz_status_string(status).decode()
+
+
+def cfz_last_error() -> str:
+    return _lib.cfz_last_error().decode(errors="replace")
+
+
+def make_desc(rows, cols, bits=4, group=64, ef_mode=CFZ_EF_DELTA, role=CFZ_SENDER) -> cfz_desc:
+    return cfz_desc(rows, cols, bits, group, ef_mode, role)
+
+
+def cfz_codes_bytes(desc: cfz_desc) -> int:
+    return _lib.cfz_codes_bytes(C.byref(desc))
+
+
+def cfz_scales_bytes(desc: cfz_desc) -> int:
+    return _lib.cfz_scales_bytes(C.byref(desc))
+
+
+def cfz_state_create(desc: cfz_desc, prev=None, base=None, err=None, x0=None, stream=None):
+    bufs = cfz_buffers(_bf16_ptr(prev), _ptr(base), _ptr(err))
+    out = C.c_void_p()
+    _check(_lib.cfz_state_create(C.byref(desc), C.byref(bufs), _bf16_ptr(x0), _stream(stream),
+                                 C.byref(out)), "cfz_state_create")
+    return out.value
+
+
+def cfz_state_resume(desc: cfz_desc, prev=None, base=None, err=None, steps=0):
+    bufs = cfz_buffers(_bf16_ptr(prev), _ptr(base), _ptr(err))
+    out = C.c_void_p()
+    _check(_lib.cfz_state_resume(C.byref(desc), C.byref(bufs), steps, C.byref(out)),
+           "cfz_state_resume")
+    return out.value
+
+
+def cfz_state_destroy(handle) -> None:
+    _check(_lib.cfz_state_destroy(handle), "cfz_state_destroy")
+
+
+def cfz_state_steps(handle) -> int:
+    return _lib.cfz_state_steps(handle)
+
+
+def cfz_compress(handle, x, codes, scales, stream=None) -> None:
+    _check(_lib.cfz_compress(handle, _bf16_ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
+           "cfz_compress")
+
+
+def cfz_decompress(handle, codes, scales, xhat=None, stream=None) -> None:
+    _check(_lib.cfz_decompress(handle, _ptr(codes), _ptr(scales), _bf16_ptr(xhat),
+                               _stream(stream)), "cfz_decompress")
+
+
+def cfz_lowrank_workspace_bytes(batch, m, n, r) -> int:
+    return _lib.cfz_lowrank_workspace_bytes(batch, m, n, r)
+
+
+def cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cfz_lowrank(batch, m, n, r, T, _bf16_ptr(A), _ptr(Q0), _ptr(U), _ptr(V),
+                            _ptr(RU), _ptr(workspace), ws_bytes, _stream(stream)), "cfz_lowrank")
+
+
+def cfz_stream_copy(src, dst, nbytes=None, stream=None) -> None:
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    _check(_lib.cfz_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "cfz_stream_copy")
+
+
+# ------------------------------------------------------------------ torch-owned state helpers
+
+class Sender:
+    """A sender's codec state with its buffers held in torch device tensors."""
+
+    def __init__(self, rows, cols, bits=4, group=64, mode=CFZ_EF_DELTA, x0=None,
+                 device="cuda", stream=None):
+        self.desc = make_desc(rows, cols, bits, group, mode, CFZ_SENDER)
+        n = rows * cols
+        self.prev = torch.empty(n, dtype=torch.bfloat16, device=device) if mode == CFZ_EF_DELTA else None
+        self.base = torch.empty(n, dtype=torch.float32, device=device) if mode != CFZ_EF_DELTA else None
+        self.err = torch.empty(n, dtype=torch.float32, device=device) if mode != CFZ_EF_OFF else None
+        self.codes = torch.empty(cfz_codes_bytes(self.desc), dtype=torch.uint8, device=device)
+        self.scales = torch.empty(n // group, dtype=torch.float32, device=device)
+        self.handle = cfz_state_create(self.desc, self.prev, self.base, self.err, x0, stream)
+
+    def compress(self, x, codes=None, scales=None, stream=None):
+        codes = self.codes if codes is None else codes
+        scales = self.scales if scales is None else scales
+        cfz_compress(self.handle, x, codes, scales, stream)
+        return codes, scales
+
+    def close(self):
+        if self.handle:
+            cfz_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Receiver:
+    """A receiver's codec state (the running base) held in a torch device tensor."""
+
+    def __init__(self, rows, cols, bits=4, group=64, x0=None, device="cuda", stream=None):
+        self.desc = make_desc(rows, cols, bits, group, CFZ_EF_DELTA, CFZ_RECEIVER)
+        self.base = torch.empty(rows * cols, dtype=torch.float32, device=device)
+        self.handle = cfz_state_create(self.desc, None, self.base, None, x0, stream)
+
+    def decompress(self, codes, scales, xhat=None, stream=None):
+        cfz_decompress(self.handle, codes, scales, xhat, stream)
+        return xhat
+
+    def close(self):
+        if self.handle:
+            cfz_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,310 @@
+// cfz_api.hip -- the C ABI of libcfz: argument validation, state handles,
+// status strings and kernel dispatch.  Nothing here touches the device until
+// every argument has been checked; a non-OK status means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "cfz.h"
+#include "cfz_internal.h"
+
+namespace {
+
+constexpr uint32_t kMagic = 0x43465a31u;  // "CFZ1"
+
+thread_local char g_last_error[512] = "";
+
+cfz_status fail(cfz_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+cfz_status fail(cfz_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+cfz_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(CFZ_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+cfz_status check_desc(const cfz_desc *d)
+{
+    if (!d)
+        return fail(CFZ_ERR_NULL, "descriptor is NULL");
+    if (d->rows < 0 || d->cols < 0)
+        return fail(CFZ_ERR_SHAPE, "negative shape %lld x %lld", (long long)d->rows,
+                    (long long)d->cols);
+    if (d->bits != 2 && d->bits != 4)
+        return fail(CFZ_ERR_UNSUPPORTED, "bits = %d (supported: 2, 4)", d->bits);
+    if (d->group != 8 && d->group != 16 && d->group != 32 && d->group != 64 && d->group != 128)
+        return fail(CFZ_ERR_UNSUPPORTED, "group = %d (supported: 8, 16, 32, 64, 128)", d->group);
+    if (d->cols % d->group != 0)
+        return fail(CFZ_ERR_SHAPE, "cols = %lld is not a multiple of group = %d",
+                    (long long)d->cols, d->group);
+    if (d->cols != 0 && d->rows > INT64_MAX / 16 / d->cols)
+        return fail(CFZ_ERR_SHAPE, "tensor too large");
+    if (d->ef_mode < CFZ_EF_DELTA || d->ef_mode > CFZ_EF_OFF)
+        return fail(CFZ_ERR_MODE, "ef_mode = %d", d->ef_mode);
+    if (d->role != CFZ_SENDER && d->role != CFZ_RECEIVER)
+        return fail(CFZ_ERR_MODE, "role = %d", d->role);
+    return CFZ_OK;
+}
+
+bool needs_prev(const cfz_desc &d) { return d.role == CFZ_SENDER && d.ef_mode == CFZ_EF_DELTA; }
+bool needs_base(const cfz_desc &d)
+{
+    return d.role == CFZ_RECEIVER || d.ef_mode == CFZ_EF_LITERAL || d.ef_mode == CFZ_EF_OFF;
+}
+bool needs_err(const cfz_desc &d)
+{
+    return d.role == CFZ_SENDER && (d.ef_mode == CFZ_EF_DELTA || d.ef_mode == CFZ_EF_LITERAL);
+}
+
+cfz_status check_buffers(const cfz_desc &d, const cfz_buffers *b, cfz_buffers *used)
+{
+    if (!b)
+        return fail(CFZ_ERR_NULL, "buffers is NULL");
+    const bool empty = d.rows * d.cols == 0;
+    *used = cfz_buffers{needs_prev(d) ? b->prev_bf16 : nullptr, needs_base(d) ? b->base_f32 : nullptr,
+                        needs_err(d) ? b->err_f32 : nullptr};
+    if (needs_prev(d) && !b->prev_bf16 && !empty)
+        return fail(CFZ_ERR_NULL, "prev_bf16 is required by a DELTA sender");
+    if (needs_base(d) && !b->base_f32 && !empty)
+        return fail(CFZ_ERR_NULL, "base_f32 is required by this role/mode");
+    if (needs_err(d) && !b->err_f32 && !empty)
+        return fail(CFZ_ERR_NULL, "err_f32 is required by this mode");
+    if (!aligned16(used->prev_bf16) || !aligned16(used->base_f32) || !aligned16(used->err_f32))
+        return fail(CFZ_ERR_ALIGN, "state buffers must be 16-byte aligned");
+    return CFZ_OK;
+}
+
+}  // namespace
+
+struct cfz_state {
+    uint32_t magic;
+    cfz_desc desc;
+    cfz_buffers bufs;
+    int64_t steps;
+};
+
+static cfz_status check_state(const cfz_state *s)
+{
+    if (!s)
+        return fail(CFZ_ERR_NULL, "state is NULL");
+    if (s->magic != kMagic)
+        return fail(CFZ_ERR_NULL, "not a live cfz_state handle");
+    return CFZ_OK;
+}
+
+extern "C" {
+
+int cfz_abi_version(void) { return CFZ_ABI_VERSION; }
+
+const char *cfz_last_error(void) { return g_last_error; }
+
+const char *cfz_status_string(cfz_status st)
+{
+    switch (st) {
+    case CFZ_OK: return "ok";
+    case CFZ_ERR_NULL: return "required pointer is NULL";
+    case CFZ_ERR_SHAPE: return "invalid shape";
+    case CFZ_ERR_UNSUPPORTED: return "unsupported bits or group";
+    case CFZ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case CFZ_ERR_MODE: return "invalid mode or role for this call";
+    case CFZ_ERR_WORKSPACE: return "workspace missing or too small";
+    case CFZ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t cfz_codes_bytes(const cfz_desc *d)
+{
+    if (check_desc(d) != CFZ_OK)
+        return 0;
+    return (size_t)(d->rows * d->cols * d->bits / 8);
+}
+
+size_t cfz_scales_bytes(const cfz_desc *d)
+{
+    if (check_desc(d) != CFZ_OK)
+        return 0;
+    return (size_t)(d->rows * d->cols / d->group) * sizeof(float);
+}
+
+cfz_status cfz_state_resume(const cfz_desc *desc, const cfz_buffers *bufs, int64_t steps,
+                            cfz_state **out)
+{
+    cfz_status st = check_desc(desc);
+    if (st != CFZ_OK)
+        return st;
+    if (!out)
+        return fail(CFZ_ERR_NULL, "out is NULL");
+    if (steps < 0)
+        return fail(CFZ_ERR_SHAPE, "steps = %lld", (long long)steps);
+    cfz_buffers used;
+    if ((st = check_buffers(*desc, bufs, &used)) != CFZ_OK)
+        return st;
+    cfz_state *s = new (std::nothrow) cfz_state{kMagic, *desc, used, steps};
+    if (!s)
+        return fail(CFZ_ERR_NULL, "out of host memory");
+    *out = s;
+    return CFZ_OK;
+}
+
+cfz_status cfz_state_create(const cfz_desc *desc, const cfz_buffers *bufs, const uint16_t *x0,
+                            void *stream, cfz_state **out)
+{
+    cfz_status st = check_desc(desc);
+    if (st != CFZ_OK)
+        return st;
+    if (!out)
+        return fail(CFZ_ERR_NULL, "out is NULL");
+    cfz_buffers used;
+    if ((st = check_buffers(*desc, bufs, &used)) != CFZ_OK)
+        return st;
+    if (!aligned16(x0))
+        return fail(CFZ_ERR_ALIGN, "x0 must be 16-byte aligned");
+    cfz_state *s = new (std::nothrow) cfz_state{kMagic, *desc, used, 0};
+    if (!s)
+        return fail(CFZ_ERR_NULL, "out of host memory");
+    const int64_t nchunks = desc->rows * desc->cols / 8;
+    hipError_t e = cfz::launch_warmup(x0, used.prev_bf16, used.base_f32, used.err_f32, nchunks,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) {
+        s->magic = 0;
+        delete s;
+        return hip_fail(e, "warm-up launch");
+    }
+    *out = s;
+    return CFZ_OK;
+}
+
+cfz_status cfz_state_destroy(cfz_state *s)
+{
+    if (!s)
+        return CFZ_OK;
+    cfz_status st = check_state(s);
+    if (st != CFZ_OK)
+        return st;
+    s->magic = 0;
+    delete s;
+    return CFZ_OK;
+}
+
+int64_t cfz_state_steps(const cfz_state *s)
+{
+    if (check_state(s) != CFZ_OK)
+        return -1;
+    return s->steps;
+}
+
+cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *scales,
+                        void *stream)
+{
+    cfz_status st = check_state(s);
+    if (st != CFZ_OK)
+        return st;
+    const cfz_desc &d = s->desc;
+    if (d.role != CFZ_SENDER)
+        return fail(CFZ_ERR_MODE, "cfz_compress needs a sender state");
+    const int64_t n = d.rows * d.cols;
+    if (n != 0 && (!x || !codes || !scales))
+        return fail(CFZ_ERR_NULL, "x, codes and scales are required");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+        return fail(CFZ_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
+    cfz::CompressArgs a{x, s->bufs.prev_bf16, s->bufs.base_f32, s->bufs.err_f32, codes, scales,
+                        n / 8, d.bits, d.group, d.ef_mode};
+    hipError_t e = cfz::launch_compress(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "compress launch");
+    ++s->steps;
+    return CFZ_OK;
+}
+
+cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scales,
+                          uint16_t *xhat, void *stream)
+{
+    cfz_status st = check_state(s);
+    if (st != CFZ_OK)
+        return st;
+    const cfz_desc &d = s->desc;
+    if (d.role != CFZ_RECEIVER)
+        return fail(CFZ_ERR_MODE, "cfz_decompress needs a receiver state");
+    const int64_t n = d.rows * d.cols;
+    if (n != 0 && (!codes || !scales))
+        return fail(CFZ_ERR_NULL, "codes and scales are required");
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(xhat))
+        return fail(CFZ_ERR_ALIGN, "codes, scales and xhat must be 16-byte aligned");
+    cfz::DecodeArgs a{codes, scales, s->bufs.base_f32, xhat, n / 8, d.bits, d.group};
+    hipError_t e = cfz::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode launch");
+    ++s->steps;
+    return CFZ_OK;
+}
+
+size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r)
+{
+    if (batch < 0 || m <= 0 || n <= 0 || r < 1 || r > 32 || r > m || r > n)
+        return 0;
+    return cfz::lowrank_workspace_bytes(batch, m, n, r);
+}
+
+cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                       const uint16_t *A, const float *Q0, float *U, float *V, float *RU,
+                       void *ws, size_t ws_bytes, void *stream)
+{
+    if (batch < 0 || m <= 0 || n <= 0)
+        return fail(CFZ_ERR_SHAPE, "batch = %lld, m = %lld, n = %lld", (long long)batch,
+                    (long long)m, (long long)n);
+    if (r < 1 || r > 32 || r > m || r > n)
+        return fail(CFZ_ERR_SHAPE, "rank r = %d must be in [1, min(32, m, n)]", r);
+    if (T < 0)
+        return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
+    if (m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
+        return fail(CFZ_ERR_SHAPE, "sizes too large");
+    if (batch == 0)
+        return CFZ_OK;
+    if (!A || !Q0 || !U || !V || !RU)
+        return fail(CFZ_ERR_NULL, "A, Q0, U, V and RU are required");
+    if (!aligned16(A) || !aligned16(Q0) || !aligned16(U) || !aligned16(V) || !aligned16(RU))
+        return fail(CFZ_ERR_ALIGN, "A, Q0, U, V and RU must be 16-byte aligned");
+    const size_t need = cfz::lowrank_workspace_bytes(batch, m, n, r);
+    if (!ws || ws_bytes < need)
+        return fail(CFZ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws & 255u) != 0)
+        return fail(CFZ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    cfz::LowrankArgs a{batch, m, n, r, T, A, Q0, U, V, RU, ws};
+    hipError_t e = cfz::launch_lowrank(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "low-rank launch");
+    return CFZ_OK;
+}
+
+cfz_status cfz_stream_copy(const void *src, void *dst, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return CFZ_OK;
+    if (!src || !dst)
+        return fail(CFZ_ERR_NULL, "src and dst are required");
+    if ((bytes & 15u) != 0)
+        return fail(CFZ_ERR_SHAPE, "bytes must be a multiple of 16");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(CFZ_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    hipError_t e = cfz::launch_stream_copy(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "copy launch");
+    return CFZ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// cfz_internal.h -- declarations shared by the sources of libcfz only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cfz {
+
+enum { kDelta = 0, kLiteral = 1, kOff = 2 };
+
+struct CompressArgs {
+    const uint16_t *x;
+    uint16_t *prev;
+    float *base;
+    float *err;
+    uint8_t *codes;
+    float *scales;
+    int64_t nchunks;  // elements / 8
+    int bits, group, mode;
+};
+
+struct DecodeArgs {
+    const uint8_t *codes;
+    const float *scales;
+    float *base;
+    uint16_t *xhat;  // may be null
+    int64_t nchunks;
+    int bits, group;
+};
+
+hipError_t launch_compress(const CompressArgs &a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, float *base, float *err,
+                         int64_t nchunks, hipStream_t st);
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t nvec, hipStream_t st);
+
+struct LowrankArgs {
+    int64_t batch, m, n;
+    int r, T;
+    const uint16_t *A;
+    const float *Q0;
+    float *U, *V, *RU;
+    void *ws;
+};
+size_t lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int r);
+hipError_t launch_lowrank(const LowrankArgs &a, hipStream_t st);
+
+}  // namespace cfz

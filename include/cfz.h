@@ -1,0 +1,169 @@
+/*
+ * cfz.h -- C ABI of libcfz, the CompactFusion residual-compression codec and
+ * rank-r subspace-iteration compressor for one AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Accelerating Parallel Diffusion Model Serving with Residual
+ * Compression" (Luo et al., NeurIPS 2025).  Parallel diffusion serving
+ * exchanges large activations (K/V or patch features) between devices at every
+ * denoising step; adjacent steps are nearly identical, so only a compressed
+ * step-wise residual is sent, with error feedback so that compression error
+ * does not accumulate (abstract; xDiT issue #573).  One uncompressed warm-up
+ * step initialises the base tensor that later residuals are taken against
+ * (reproducibility table, "Dataset Splits").  A rank-r compressor by subspace
+ * iteration is given as Algorithm 3 (reproducibility table, "Pseudocode").
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned, contiguous, row-major and 16-byte
+ *     aligned.  The library never allocates device memory.
+ *   - bf16 values travel as raw uint16_t bit patterns.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  No call synchronises.  Buffers must stay alive
+ *     until the enqueued work has finished.
+ *   - All arguments are validated before anything is enqueued: a non-OK
+ *     status means no device work was queued and no buffer was written.
+ *     A failed launch returns CFZ_ERR_HIP.  No C++ exception crosses the ABI.
+ *     cfz_last_error() gives a thread-local description of the last failure.
+ *   - A cfz_state is a small host object.  It must not be used on two
+ *     streams at once; the caller's stream order is the step order.
+ */
+#ifndef CFZ_H
+#define CFZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CFZ_ABI_VERSION 1
+
+typedef enum {
+    CFZ_OK = 0,
+    CFZ_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    CFZ_ERR_SHAPE = 2,       /* negative size, cols % group != 0, m/n/r/T out of range */
+    CFZ_ERR_UNSUPPORTED = 3, /* bits not in {2, 4}, group not in {8,16,32,64,128}  */
+    CFZ_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned             */
+    CFZ_ERR_MODE = 5,        /* bad ef_mode/role, or the call does not fit the role */
+    CFZ_ERR_WORKSPACE = 6,   /* low-rank workspace missing or too small             */
+    CFZ_ERR_HIP = 7          /* the HIP runtime reported an error                   */
+} cfz_status;
+
+/* How the sender forms the residual and carries the compression error.
+ *   DELTA   (default): r = (x - prev) + err; prev' = x; err' = r - q s.
+ *           Error feedback on step-wise activation differences: the receiver's
+ *           base then equals x - err' after every step.
+ *   LITERAL: r = (x - base) + err; err' = r - q s; base' = base + q s.
+ *           The carried error is added on top of a base that already absorbs
+ *           it; kept to reproduce that reading, which is unstable at 2 bits.
+ *   OFF:     r = x - base; base' = base + q s (closed loop, no error buffer).
+ * The receiver always does base' = base + q s. */
+typedef enum { CFZ_EF_DELTA = 0, CFZ_EF_LITERAL = 1, CFZ_EF_OFF = 2 } cfz_ef_mode;
+
+typedef enum { CFZ_SENDER = 0, CFZ_RECEIVER = 1 } cfz_role;
+
+/* One exchanged tensor: rows (tokens) x cols (channels), quantized in groups of
+ * `group` consecutive channels of one row with `bits`-bit codes.
+ * Requirements: rows >= 0, cols >= 0, bits in {2, 4}, group in {8,16,32,64,128},
+ * cols % group == 0.  rows * cols == 0 is allowed (every call is then a no-op). */
+typedef struct {
+    int64_t rows;
+    int64_t cols;
+    int32_t bits;
+    int32_t group;
+    int32_t ef_mode; /* cfz_ef_mode */
+    int32_t role;    /* cfz_role    */
+} cfz_desc;
+
+/* Caller-owned state buffers, rows*cols elements each, on the device.
+ *   prev_bf16: sender in DELTA mode (previous activation, bf16).
+ *   base_f32:  receiver; sender in LITERAL and OFF modes (running reconstruction).
+ *   err_f32:   sender in DELTA and LITERAL modes (carried error).
+ * Buffers the role/mode does not use are ignored and may be NULL. */
+typedef struct {
+    uint16_t *prev_bf16;
+    float *base_f32;
+    float *err_f32;
+} cfz_buffers;
+
+typedef struct cfz_state cfz_state;
+
+/* Warm-up (step 0): the uncompressed activation x0 initialises the state.
+ * Receiver: base = fp32(x0).  Sender: prev = x0 (DELTA), base = fp32(x0)
+ * (LITERAL, OFF), err = 0 (DELTA, LITERAL).  x0 == NULL means all zeros.
+ * Enqueues one initialisation kernel on hip_stream, then returns the handle.
+ * On error *out is left unchanged.  (paper: reproducibility table,
+ * "Dataset Splits" -- warm-up initialises the base tensor.) */
+cfz_status cfz_state_create(const cfz_desc *desc, const cfz_buffers *bufs,
+                            const uint16_t *x0_bf16, void *hip_stream, cfz_state **out);
+
+/* Rebuild a handle around buffers that already hold a state (checkpoint/resume).
+ * Enqueues nothing.  `steps` is the number of compressed steps already taken. */
+cfz_status cfz_state_resume(const cfz_desc *desc, const cfz_buffers *bufs, int64_t steps,
+                            cfz_state **out);
+
+/* Frees the host handle only; the caller owns and frees the device buffers.
+ * NULL is accepted. */
+cfz_status cfz_state_destroy(cfz_state *state);
+
+/* Number of compressed steps enqueued on this state so far (-1 for NULL). */
+int64_t cfz_state_steps(const cfz_state *state);
+
+/* Payload sizes for one step: codes rows*cols*bits/8 bytes, scales
+ * rows*cols/group fp32 values (bytes returned).  0 for an invalid descriptor. */
+size_t cfz_codes_bytes(const cfz_desc *desc);
+size_t cfz_scales_bytes(const cfz_desc *desc);
+
+/* One compressed step at the sender, fused in one kernel: residual with error
+ * feedback, group absmax scale s = max|r| / qmax (qmax = 2^(bits-1) - 1, IEEE
+ * fp32 division), q = clamp(rint(r / s), -qmax, qmax) (0 when s == 0), packing
+ * of q into bits-bit two's complement fields (element j in byte j*bits/8 at
+ * bit (j*bits) % 8), and the state update of the sender's ef_mode.
+ * x: rows*cols bf16.  codes: cfz_codes_bytes.  scales: rows*cols/group fp32,
+ * scale k covering elements [k*group, (k+1)*group).
+ * (paper: abstract -- compressed step-wise residuals with error feedback.)
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_ALIGN, CFZ_ERR_MODE (receiver state), CFZ_ERR_HIP. */
+cfz_status cfz_compress(cfz_state *sender, const uint16_t *x_bf16, uint8_t *codes,
+                        float *scales, void *hip_stream);
+
+/* One step at the receiver: unpack, sign-extend, base' = fma(q, s, base) where
+ * q != 0 (a zero code leaves the base bit-identical), and optionally write the
+ * new base rounded to bf16 (nearest even) into xhat_bf16 (may be NULL).
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_ALIGN, CFZ_ERR_MODE (sender state), CFZ_ERR_HIP. */
+cfz_status cfz_decompress(cfz_state *receiver, const uint8_t *codes, const float *scales,
+                          uint16_t *xhat_bf16, void *hip_stream);
+
+/* Workspace for cfz_lowrank, in bytes, or 0 if the sizes are invalid. */
+size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r);
+
+/* Algorithm 3 (Subspace Iteration, rank r) on `batch` independent matrices
+ * (paper: reproducibility table, "Pseudocode", Algorithm 3):
+ *   Q = orth(Q0); T times { Z = A^T (A Q); Q = orth(Z) }; (U, R_U) = orth(A Q); V = Q.
+ * orth() is a thin QR with positive diagonal (Cholesky-QR applied twice, Gram
+ * matrix and r x r Cholesky in fp64); a column whose pivot is <= 1e-13 of the
+ * mean squared column norm is dropped (zero column of Q, zero row and column
+ * of R).  The reconstruction of A is U R_U V^T = (A Q) Q^T.
+ * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn).
+ * U: [batch][m][r], V: [batch][n][r], RU: [batch][r][r], fp32 outputs.
+ * Requires 1 <= r <= 32, r <= m, r <= n, T >= 0, m, n multiples of 32 and
+ * n <= 65536, batch >= 0 (0 is a no-op); workspace of
+ * cfz_lowrank_workspace_bytes(batch, m, n, r) bytes, 256-byte aligned.
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_WORKSPACE, CFZ_ERR_HIP. */
+cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                       const uint16_t *A_bf16, const float *Q0, float *U, float *V, float *RU,
+                       void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* Measurement aid: a plain streaming copy of `bytes` bytes (multiple of 16,
+ * both pointers 16-byte aligned) on hip_stream, used to calibrate HBM
+ * traffic counters and the achievable copy bandwidth.  Not part of the codec. */
+cfz_status cfz_stream_copy(const void *src, void *dst, size_t bytes, void *hip_stream);
+
+const char *cfz_status_string(cfz_status status);
+const char *cfz_last_error(void);
+int cfz_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFZ_H */

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (include/cfz.h) that need no GPU: the library
+loads, exports every declared function, and rejects bad arguments with the
+documented status before it would enqueue any device work.  Every call below
+fails validation or touches host memory only."""
+import ctypes as C
+
+import pytest
+
+from diffusion_activation_residual_amd import cfz
+
+ALIGNED = 0x10000      # fake device addresses: never dereferenced, since validation fails first
+MISALIGNED = 0x10008
+
+
+def test_library_exports_every_declared_function():
+    names = cfz.header_functions()
+    assert len(names) == 14
+    for name in names:
+        assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
+    assert cfz.cfz_abi_version() == 1
+
+
+def test_status_strings():
+    for st in range(8):
+        assert cfz.cfz_status_string(st)
+    assert cfz.cfz_status_string(99) == "unknown status"
+
+
+def test_payload_sizes():
+    d = cfz.make_desc(1024, 3072, 4, 64)
+    assert cfz.cfz_codes_bytes(d) == 1024 * 3072 // 2
+    assert cfz.cfz_scales_bytes(d) == 1024 * 3072 // 64 * 4
+    d = cfz.make_desc(4388, 1920, 2, 32)
+    assert cfz.cfz_codes_bytes(d) == 4388 * 1920 // 4
+    assert cfz.cfz_scales_bytes(d) == 4388 * 1920 // 32 * 4
+    assert cfz.cfz_codes_bytes(cfz.make_desc(10, 100, 4, 64)) == 0  # cols % group != 0
+
+
+def _create_status(desc, bufs, x0=None):
+    out = C.c_void_p(0xdead)
+    st = cfz._lib.cfz_state_create(C.byref(desc) if desc is not None else None,
+                                   C.byref(bufs) if bufs is not None else None, x0, None,
+                                   C.byref(out))
+    assert out.value == 0xdead, "output handle written on failure"
+    return st
+
+
+@pytest.mark.parametrize("desc,status", [
+    (cfz.make_desc(-1, 64), cfz.CFZ_ERR_SHAPE),
+    (cfz.make_desc(4, 64, bits=3), cfz.CFZ_ERR_UNSUPPORTED),
+    (cfz.make_desc(4, 64, bits=8), cfz.CFZ_ERR_UNSUPPORTED),
+    (cfz.make_desc(4, 96, group=48), cfz.CFZ_ERR_UNSUPPORTED),
+    (cfz.make_desc(4, 96, group=256), cfz.CFZ_ERR_UNSUPPORTED),
+    (cfz.make_desc(4, 96, group=64), cfz.CFZ_ERR_SHAPE),
+    (cfz.make_desc(4, 64, ef_mode=3), cfz.CFZ_ERR_MODE),
+    (cfz.make_desc(4, 64, role=2), cfz.CFZ_ERR_MODE),
+])
+def test_create_rejects_bad_descriptor(desc, status):
+    bufs = cfz.cfz_buffers(ALIGNED, ALIGNED, ALIGNED)
+    assert _create_status(desc, bufs) == status
+    assert cfz.cfz_last_error()
+
+
+def test_create_rejects_missing_or_misaligned_buffers():
+    assert _create_status(None, cfz.cfz_buffers()) == cfz.CFZ_ERR_NULL
+    d = cfz.make_desc(4, 64)
+    assert _create_status(d, None) == cfz.CFZ_ERR_NULL
+    # DELTA sender needs prev and err
+    assert _create_status(d, cfz.cfz_buffers(None, None, ALIGNED)) == cfz.CFZ_ERR_NULL
+    assert _create_status(d, cfz.cfz_buffers(ALIGNED, None, None)) == cfz.CFZ_ERR_NULL
+    assert _create_status(d, cfz.cfz_buffers(MISALIGNED, None, ALIGNED)) == cfz.CFZ_ERR_ALIGN
+    assert _create_status(d, cfz.cfz_buffers(ALIGNED, None, ALIGNED), x0=MISALIGNED) == \
+        cfz.CFZ_ERR_ALIGN
+    # receiver needs base
+    r = cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER)
+    assert _create_status(r, cfz.cfz_buffers(ALIGNED, None, ALIGNED)) == cfz.CFZ_ERR_NULL
+    # LITERAL sender needs base and err; OFF needs base
+    lit = cfz.make_desc(4, 64, ef_mode=cfz.CFZ_EF_LITERAL)
+    assert _create_status(lit, cfz.cfz_buffers(ALIGNED, None, ALIGNED)) == cfz.CFZ_ERR_NULL
+    off = cfz.make_desc(4, 64, ef_mode=cfz.CFZ_EF_OFF)
+    assert _create_status(off, cfz.cfz_buffers(ALIGNED, None, ALIGNED)) == cfz.CFZ_ERR_NULL
+
+
+def test_resume_handle_lifecycle_and_role_checks():
+    """cfz_state_resume enqueues nothing, so its handles can be exercised on the host."""
+    snd = cfz.cfz_state_resume(cfz.make_desc(4, 64), prev=ALIGNED, err=ALIGNED, steps=5)
+    rcv = cfz.cfz_state_resume(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER), base=ALIGNED, steps=5)
+    try:
+        assert cfz.cfz_state_steps(snd) == 5
+        lib = cfz._lib
+        # wrong role: no launch
+        assert lib.cfz_compress(rcv, ALIGNED, ALIGNED, ALIGNED, None) == cfz.CFZ_ERR_MODE
+        assert lib.cfz_decompress(snd, ALIGNED, ALIGNED, None, None) == cfz.CFZ_ERR_MODE
+        # missing or misaligned payload pointers: no launch
+        assert lib.cfz_compress(snd, None, ALIGNED, ALIGNED, None) == cfz.CFZ_ERR_NULL
+        assert lib.cfz_compress(snd, ALIGNED, MISALIGNED, ALIGNED, None) == cfz.CFZ_ERR_ALIGN
+        assert lib.cfz_decompress(rcv, ALIGNED, None, None, None) == cfz.CFZ_ERR_NULL
+        assert lib.cfz_decompress(rcv, ALIGNED, ALIGNED, MISALIGNED, None) == cfz.CFZ_ERR_ALIGN
+        assert cfz.cfz_state_steps(snd) == 5 and cfz.cfz_state_steps(rcv) == 5
+        assert lib.cfz_compress(None, ALIGNED, ALIGNED, ALIGNED, None) == cfz.CFZ_ERR_NULL
+        assert cfz.cfz_state_steps(None) == -1
+    finally:
+        cfz.cfz_state_destroy(snd)
+        cfz.cfz_state_destroy(rcv)
+    cfz.cfz_state_destroy(None)
+    with pytest.raises(cfz.CfzError):
+        cfz.cfz_state_resume(cfz.make_desc(4, 64), prev=ALIGNED, err=ALIGNED, steps=-1)
+
+
+def test_lowrank_validation():
+    lib = cfz._lib
+    ws_need = cfz.cfz_lowrank_workspace_bytes(2, 128, 192, 8)
+    assert ws_need > 0
+    assert cfz.cfz_lowrank_workspace_bytes(2, 128, 192, 33) == 0
+    assert cfz.cfz_lowrank_workspace_bytes(2, 4, 192, 8) == 0
+
+    def call(batch=2, m=128, n=192, r=8, T=2, A=ALIGNED, Q0=ALIGNED, U=ALIGNED, V=ALIGNED,
+             RU=ALIGNED, ws=ALIGNED, ws_bytes=None):
+        return lib.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws,
+                               ws_need if ws_bytes is None else ws_bytes, None)
+
+    assert call(r=0) == cfz.CFZ_ERR_SHAPE
+    assert call(r=33) == cfz.CFZ_ERR_SHAPE
+    assert call(T=-1) == cfz.CFZ_ERR_SHAPE
+    assert call(m=0) == cfz.CFZ_ERR_SHAPE
+    assert call(batch=-1) == cfz.CFZ_ERR_SHAPE
+    assert call(A=None) == cfz.CFZ_ERR_NULL
+    assert call(RU=None) == cfz.CFZ_ERR_NULL
+    assert call(U=MISALIGNED) == cfz.CFZ_ERR_ALIGN
+    assert call(ws=None) == cfz.CFZ_ERR_WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == cfz.CFZ_ERR_WORKSPACE
+    assert call(ws=ALIGNED + 16) == cfz.CFZ_ERR_ALIGN
+    assert call(batch=0, A=None) == cfz.CFZ_OK  # empty batch: no-op
+
+
+def test_stream_copy_validation():
+    lib = cfz._lib
+    assert lib.cfz_stream_copy(None, ALIGNED, 16, None) == cfz.CFZ_ERR_NULL
+    assert lib.cfz_stream_copy(ALIGNED, ALIGNED, 17, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_stream_copy(MISALIGNED, ALIGNED, 16, None) == cfz.CFZ_ERR_ALIGN
+    assert lib.cfz_stream_copy(None, None, 0, None) == cfz.CFZ_OK
+
+
+def test_binding_has_same_names_as_header():
+    for name in cfz.header_functions():
+        assert hasattr(cfz, name), f"binding lacks {name}"

@@ -1,0 +1,333 @@
+"""GPU parity of the HIP codec (through the C ABI) against the CPU oracle.
+
+Bar: packed codes and fp32 scales bit-exact; error buffer, previous activation,
+bases and bf16 reconstructions bit-exact as well (both sides use IEEE fp32
+division, ties-to-even rounding and the same two explicit fma operations).
+Inputs: seeded AR(1) activations at the workload shapes (synth module)."""
+import ctypes as C
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import SPECS, AR1Stream
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from diffusion_activation_residual_amd import cfz
+DEV = "cuda:0"
+
+MODE_PAIRS = {0: oracle.DELTA, 1: oracle.LITERAL, 2: oracle.OFF}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+
+def u32(t):
+    return t.contiguous().cpu().numpy().view(np.uint32).reshape(-1)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _compare_step(tag, gs, gr, codes, scales, os_, or_, ocodes, oscales, xhat=None, oxhat=None):
+    assert np.array_equal(codes.cpu().numpy(), ocodes), f"{tag}: codes"
+    assert np.array_equal(u32(scales), oscales.view(np.uint32)), f"{tag}: scales"
+    if os_.err is not None:
+        assert np.array_equal(u32(gs.err), os_.err.view(np.uint32)), f"{tag}: err"
+    if os_.prev is not None:
+        assert np.array_equal(u16(gs.prev), os_.prev), f"{tag}: prev"
+    if os_.base is not None:
+        assert np.array_equal(u32(gs.base), os_.base.view(np.uint32)), f"{tag}: sender base"
+    assert np.array_equal(u32(gr.base), or_.base.view(np.uint32)), f"{tag}: receiver base"
+    if xhat is not None:
+        assert np.array_equal(u16(xhat), oxhat), f"{tag}: xhat"
+
+
+def _run_parity(xs, rows, cols, bits, group, mode, tag, want_xhat=True):
+    """xs: list of bf16 CPU tensors [rows, cols]; step 0 is the warm-up."""
+    n = rows * cols
+    say(f"[gpu] {tag}: rows={rows} cols={cols} bits={bits} group={group} mode={mode}")
+    gs = cfz.Sender(rows, cols, bits, group, mode, x0=xs[0].to(DEV))
+    gr = cfz.Receiver(rows, cols, bits, group, x0=xs[0].to(DEV))
+    os_ = oracle.Sender(n, bits, group, MODE_PAIRS[mode], x0=u16(xs[0]))
+    or_ = oracle.Receiver(n, bits, group, x0=u16(xs[0]))
+    xhat = torch.empty(n, dtype=torch.bfloat16, device=DEV) if want_xhat else None
+    for t in range(1, len(xs)):
+        codes, scales = gs.compress(xs[t].to(DEV))
+        gr.decompress(codes, scales, xhat)
+        ocodes, oscales = os_.compress(u16(xs[t]))
+        oxhat = or_.decompress(ocodes, oscales, want_xhat=want_xhat)
+        torch.cuda.synchronize()
+        _compare_step(f"{tag} step {t}", gs, gr, codes, scales, os_, or_, ocodes, oscales,
+                      xhat, oxhat)
+    assert cfz.cfz_state_steps(gs.handle) == len(xs) - 1
+    gs.close()
+    gr.close()
+
+
+def _ar1(rows, cols, steps, spec="flux", seed=0, n_tensors=1):
+    sp = SPECS[spec]
+    st = AR1Stream(n_tensors, rows, cols, sp.alpha, sp.noise, sp.outlier_frac, seed=seed,
+                   key=f"{spec}-test")
+    return [st.next() for _ in range(steps)]
+
+
+def test_tiny_config_every_step():
+    sp = SPECS["tiny"]
+    st = AR1Stream.from_spec(sp, seed=0)
+    xs = [st.next()[0] for _ in range(sp.steps)]
+    _run_parity(xs, sp.rows, sp.cols, 4, 64, cfz.CFZ_EF_DELTA, "tiny int4 g64")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", [8, 16, 32, 64, 128])
+@pytest.mark.parametrize("bits", [4, 2])
+def test_every_variant_several_tiles_and_ragged_tail(bits, group, mode):
+    # 300 x 256 = 9600 chunks of 8: 18.75 blocks of 512 chunks, so a ragged last block
+    xs = [x[0] for x in _ar1(300, 256, 4, seed=bits * 100 + group + mode)]
+    _run_parity(xs, 300, 256, bits, group, mode, f"variant b{bits} g{group} m{mode}")
+
+
+@pytest.mark.parametrize("rows,cols,group", [(1, 8, 8), (1, 64, 64), (3, 128, 128), (5, 24, 8),
+                                             (513, 64, 32), (2, 4096, 64)])
+def test_odd_shapes(rows, cols, group):
+    xs = [x[0] for x in _ar1(rows, cols, 3, seed=rows + cols)]
+    for bits in (4, 2):
+        _run_parity(xs, rows, cols, bits, group, cfz.CFZ_EF_DELTA, f"shape {rows}x{cols}")
+
+
+def test_empty_tensor_is_a_noop():
+    say("[gpu] empty tensor")
+    s = cfz.Sender(0, 64, 4, 64)
+    r = cfz.Receiver(0, 64, 4, 64)
+    x = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    codes, scales = s.compress(x)
+    r.decompress(codes, scales)
+    torch.cuda.synchronize()
+    assert codes.numel() == 0 and scales.numel() == 0
+
+
+def test_extreme_magnitudes():
+    """Subnormal, tiny and huge groups, all-zero groups and exact ties."""
+    rng = np.random.default_rng(5)
+    rows, cols = 64, 512
+    mags = np.array([1e-38, 1e-30, 3e-39, 1.0, 1e20, 1e30, 0.0, 1e-3], np.float32)
+    sc = np.repeat(mags, cols // len(mags))
+    xs = []
+    for t in range(4):
+        v = (rng.standard_normal((rows, cols)) * sc).astype(np.float32)
+        if t == 2:
+            v[:8] = np.round(rng.uniform(-7, 7, (8, cols)) * 2) / 2  # half-integer lattice
+        xs.append(torch.from_numpy(v).to(torch.bfloat16))
+    xs[3][10:20] = xs[2][10:20]  # unchanged rows: zero residual in DELTA
+    for bits, group in ((4, 64), (2, 32), (4, 8)):
+        for mode in (0, 1, 2):
+            _run_parity(xs, rows, cols, bits, group, mode, f"extreme b{bits} g{group} m{mode}")
+
+
+def test_zero_residual_leaves_state_bitwise():
+    say("[gpu] zero residual")
+    x0 = _ar1(64, 256, 1)[0][0].to(DEV)
+    s = cfz.Sender(64, 256, 4, 64, cfz.CFZ_EF_DELTA, x0=x0)
+    r = cfz.Receiver(64, 256, 4, 64, x0=x0)
+    base0 = r.base.clone()
+    codes, scales = s.compress(x0)
+    r.decompress(codes, scales)
+    torch.cuda.synchronize()
+    assert not codes.any() and not scales.any()
+    assert not s.err.view(torch.int32).any()
+    assert torch.equal(r.base.view(torch.int32), base0.view(torch.int32))
+
+
+def test_checkpoint_resume_and_determinism():
+    rows, cols, steps, k = 128, 512, 8, 3
+    xs = [x[0].to(DEV) for x in _ar1(rows, cols, steps, seed=9)]
+    say("[gpu] checkpoint/resume")
+
+    def run_all():
+        s = cfz.Sender(rows, cols, 4, 64, cfz.CFZ_EF_DELTA, x0=xs[0])
+        outs = []
+        for t in range(1, steps):
+            c, sc = s.compress(xs[t])
+            outs.append((c.clone(), sc.clone()))
+        torch.cuda.synchronize()
+        return s, outs
+
+    s1, outs1 = run_all()
+    s2, outs2 = run_all()
+    for (a, b), (c, d) in zip(outs1, outs2):
+        assert torch.equal(a, c) and torch.equal(b.view(torch.int32), d.view(torch.int32))
+    # resume from a copy of the state after k steps
+    s3 = cfz.Sender(rows, cols, 4, 64, cfz.CFZ_EF_DELTA, x0=xs[0])
+    for t in range(1, k + 1):
+        s3.compress(xs[t])
+    prev, err = s3.prev.clone(), s3.err.clone()
+    h = cfz.cfz_state_resume(s3.desc, prev=prev, err=err, steps=k)
+    codes = torch.empty_like(s3.codes)
+    scales = torch.empty_like(s3.scales)
+    for t in range(k + 1, steps):
+        cfz.cfz_compress(h, xs[t], codes, scales)
+        torch.cuda.synchronize()
+        assert torch.equal(codes, outs1[t - 1][0])
+        assert torch.equal(scales.view(torch.int32), outs1[t - 1][1].view(torch.int32))
+    assert cfz.cfz_state_steps(h) == steps - 1
+    assert torch.equal(err.view(torch.int32), s1.err.view(torch.int32))
+    cfz.cfz_state_destroy(h)
+
+
+def test_error_paths_have_no_side_effects():
+    say("[gpu] error paths")
+    x0 = _ar1(32, 256, 1)[0][0].to(DEV)
+    s = cfz.Sender(32, 256, 4, 64, cfz.CFZ_EF_DELTA, x0=x0)
+    codes = torch.full((32 * 256 // 2 + 16,), 0x5a, dtype=torch.uint8, device=DEV)
+    scales = torch.full((32 * 256 // 64,), 3.0, device=DEV)
+    err0 = s.err.clone()
+    with pytest.raises(cfz.CfzError) as ei:
+        cfz.cfz_compress(s.handle, x0, codes[1:].data_ptr(), scales)
+    assert ei.value.status == cfz.CFZ_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert bool((codes == 0x5a).all()) and bool((scales == 3.0).all())
+    assert torch.equal(s.err, err0)
+    assert cfz.cfz_state_steps(s.handle) == 0
+
+
+def test_stream_copy_matches():
+    say("[gpu] stream copy")
+    a = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=DEV)
+    b = torch.zeros_like(a)
+    cfz.cfz_stream_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_runs_on_a_side_stream():
+    rows, cols = 256, 512
+    xs = [x[0].to(DEV) for x in _ar1(rows, cols, 3, seed=4)]
+    say("[gpu] side stream")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        s = cfz.Sender(rows, cols, 4, 64, x0=xs[0])
+        for t in (1, 2):
+            c, sc = s.compress(xs[t])
+    st.synchronize()
+    os_ = oracle.Sender(rows * cols, 4, 64, oracle.DELTA, x0=u16(xs[0]))
+    for t in (1, 2):
+        oc, osc = os_.compress(u16(xs[t]))
+    assert np.array_equal(c.cpu().numpy(), oc)
+
+
+# ------------------------------------------------------------------ full workload sizes
+
+def test_flux_int4_full_size_sampled_tensors():
+    """FLUX.1-dev share, 57 layers x {K, V} of 1024 x 3072, int4 g64, DELTA, 28 steps, in the
+    per-tensor launch configuration of the benchmark; layers 0, 28, 56 compared every step."""
+    sp = SPECS["flux"]
+    st = AR1Stream.from_spec(sp, seed=0, device=DEV)
+    picks = [0, 1, 56, 57, 112, 113]
+    say(f"[gpu] flux int4 full size, tensors {picks}")
+    x = st.next()
+    n = sp.rows * sp.cols
+    gs = [cfz.Sender(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous()) for i in picks]
+    gr = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous()) for i in picks]
+    os_ = [oracle.Sender(n, 4, 64, oracle.DELTA, x0=u16(x[i])) for i in picks]
+    or_ = [oracle.Receiver(n, 4, 64, x0=u16(x[i])) for i in picks]
+    for t in range(1, sp.steps):
+        x = st.next()
+        for j, i in enumerate(picks):
+            codes, scales = gs[j].compress(x[i].contiguous())
+            gr[j].decompress(codes, scales)
+            oc, osc = os_[j].compress(u16(x[i]))
+            or_[j].decompress(oc, osc)
+            torch.cuda.synchronize()
+            _compare_step(f"flux t{t} tensor {i}", gs[j], gr[j], codes, scales, os_[j], or_[j],
+                          oc, osc)
+
+
+def _batched_rows_parity(spec_name, bits, group, steps, row_slices, tag):
+    sp = SPECS[spec_name]
+    rows = sp.tensors * sp.rows
+    st = AR1Stream.from_spec(sp, seed=1, device=DEV)
+    say(f"[gpu] {tag}: one launch over {rows} x {sp.cols}, {steps} steps")
+    x = st.next().reshape(rows, sp.cols)
+    gs = cfz.Sender(rows, sp.cols, bits, group, x0=x)
+    gr = cfz.Receiver(rows, sp.cols, bits, group, x0=x)
+    os_, or_ = [], []
+    for a, b in row_slices:
+        xs = u16(x[a:b])
+        os_.append(oracle.Sender(xs.size, bits, group, oracle.DELTA, x0=xs))
+        or_.append(oracle.Receiver(xs.size, bits, group, x0=xs))
+    cpr = sp.cols * bits // 8   # code bytes per row
+    spr = sp.cols // group      # scales per row
+    for t in range(1, steps):
+        x = st.next().reshape(rows, sp.cols)
+        codes, scales = gs.compress(x)
+        gr.decompress(codes, scales)
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(row_slices):
+            oc, osc = os_[j].compress(u16(x[a:b]))
+            or_[j].decompress(oc, osc)
+            assert np.array_equal(codes[a * cpr:b * cpr].cpu().numpy(), oc), f"{tag} t{t} codes"
+            assert np.array_equal(u32(scales[a * spr:b * spr]), osc.view(np.uint32))
+            n0, n1 = a * sp.cols, b * sp.cols
+            assert np.array_equal(u32(gs.err[n0:n1]), os_[j].err.view(np.uint32))
+            assert np.array_equal(u16(gs.prev[n0:n1]), os_[j].prev)
+            assert np.array_equal(u32(gr.base[n0:n1]), or_[j].base.view(np.uint32))
+
+
+def test_flux_int2_batched_full_size_sampled_rows():
+    """All 57 layers' K/V (116736 x 3072 bf16, about 717 MB) in one launch per step,
+    2-bit group 32; first, middle and last rows compared every step."""
+    rows = SPECS["flux"].tensors * SPECS["flux"].rows
+    sl = [(0, 64), (rows // 2 - 32, rows // 2 + 32), (rows - 64, rows)]
+    _batched_rows_parity("flux", 2, 32, SPECS["flux"].steps, sl, "flux int2 batched")
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (2, 32)])
+def test_cogvideox_full_size_sampled_rows(bits, group):
+    """CogVideoX-2b share, 30 layers x {K, V} of 4388 x 1920 in one launch per step, 50 steps."""
+    sp = SPECS["cogvideox"]
+    rows = sp.tensors * sp.rows
+    sl = [(0, 96), (29 * sp.rows, 29 * sp.rows + 96), (rows - 96, rows)]
+    _batched_rows_parity("cogvideox", bits, group, sp.steps, sl, f"cogvideox b{bits}")
+
+
+def test_graph_replay_matches_oracle_every_replay():
+    """The benchmark replays captured per-tensor launches; every replay must advance the state
+    exactly like an eager step (checked against the oracle after each replay, with eager
+    work and synchronisations between replays)."""
+    rows, cols, steps = 256, 1024, 6
+    xs = [x[0].to(DEV) for x in _ar1(rows, cols, steps + 1, seed=12)]
+    say("[gpu] graph replay")
+    xin = torch.empty_like(xs[0])
+    gs = cfz.Sender(rows, cols, 4, 64, x0=xs[0])
+    gr = cfz.Receiver(rows, cols, 4, 64, x0=xs[0])
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        gs.compress(xin)
+        gr.decompress(gs.codes, gs.scales)
+    torch.cuda.synchronize()
+    n = rows * cols
+    os_ = oracle.Sender(n, 4, 64, oracle.DELTA, x0=u16(xs[0]))
+    or_ = oracle.Receiver(n, 4, 64, x0=u16(xs[0]))
+    for t in range(1, steps + 1):
+        xin.copy_(xs[t])                       # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        oc, osc = os_.compress(u16(xs[t]))
+        or_.decompress(oc, osc)
+        _compare_step(f"graph replay {t}", gs, gr, gs.codes, gs.scales, os_, or_, oc, osc)
