@@ -254,7 +254,8 @@ cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scale
 
 size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r)
 {
-    if (batch < 0 || m <= 0 || n <= 0 || r < 1 || r > 32 || r > m || r > n)
+    if (batch < 0 || m <= 0 || n <= 0 || r < 1 || r > 32 || r > m || r > n || n % 8 != 0 ||
+        m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
         return 0;
     return cfz::lowrank_workspace_bytes(batch, m, n, r);
 }
@@ -270,6 +271,8 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
         return fail(CFZ_ERR_SHAPE, "rank r = %d must be in [1, min(32, m, n)]", r);
     if (T < 0)
         return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
+    if (n % 8 != 0)
+        return fail(CFZ_ERR_SHAPE, "n = %lld must be a multiple of 8 (16-byte rows)", (long long)n);
     if (m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
         return fail(CFZ_ERR_SHAPE, "sizes too large");
     if (batch == 0)

@@ -145,9 +145,13 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
  * of R).  The reconstruction of A is U R_U V^T = (A Q) Q^T.
  * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn).
  * U: [batch][m][r], V: [batch][n][r], RU: [batch][r][r], fp32 outputs.
- * Requires 1 <= r <= 32, r <= m, r <= n, T >= 0, m, n multiples of 32 and
- * n <= 65536, batch >= 0 (0 is a no-op); workspace of
- * cfz_lowrank_workspace_bytes(batch, m, n, r) bytes, 256-byte aligned.
+ * Requires 1 <= r <= 32, r <= m, r <= n, T >= 0, n a multiple of 8 (rows of A
+ * are 16-byte aligned), m, n, batch <= 2^20, batch >= 0 (0 is a no-op); a
+ * workspace of cfz_lowrank_workspace_bytes(batch, m, n, r) bytes, 256-byte
+ * aligned, that the call overwrites.  Products use bf16 MFMA with fp32
+ * accumulation; Q and A Q enter them split into two bf16 halves (about 16
+ * significant bits), so U R_U V^T agrees with an fp64 evaluation to about 1e-5
+ * relative Frobenius error on well-conditioned inputs.
  * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_WORKSPACE, CFZ_ERR_HIP. */
 cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
                        const uint16_t *A_bf16, const float *Q0, float *U, float *V, float *RU,

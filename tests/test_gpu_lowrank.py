@@ -1,0 +1,157 @@
+"""GPU parity of the subspace iteration (Algorithm 3, through the C ABI) against the
+fp64 CPU oracle.  Bar: U R_U V^T, U, V and R_U within 1e-3 relative Frobenius
+error of the oracle (the columns of U and V that span a noise subspace at
+r = 32 on a rank-16 input are not unique to rounding and are excluded: only the
+leading 16 columns are compared there)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import exact_rank_batch, gaussian_q0, lowrank_batch
+
+pytestmark = pytest.mark.gpu
+if torch.cuda.is_available():
+    from diffusion_activation_residual_amd import cfz
+DEV = "cuda:0"
+TOL = 1e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def run_gpu(A, Q0, r, T):
+    batch, m, n = A.shape
+    Ad, Qd = A.to(DEV).contiguous(), Q0.to(DEV).contiguous()
+    U = torch.full((batch, m, r), float("nan"), device=DEV)
+    V = torch.full((batch, n, r), float("nan"), device=DEV)
+    RU = torch.full((batch, r, r), float("nan"), device=DEV)
+    ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(batch, m, n, r), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xff)  # NaN patterns: results must not depend on stale workspace contents
+    cfz.cfz_lowrank(batch, m, n, r, T, Ad, Qd, U, V, RU, ws)
+    torch.cuda.synchronize()
+    return U.double().cpu().numpy(), V.double().cpu().numpy(), RU.double().cpu().numpy()
+
+
+def check(A, Q0, r, T, layers=None, lead=None, tag=""):
+    batch, m, n = A.shape
+    say(f"[gpu] lowrank {tag}: batch={batch} m={m} n={n} r={r} T={T}")
+    U, V, RU = run_gpu(A, Q0, r, T)
+    for b in (range(batch) if layers is None else layers):
+        ou, ov, oru = oracle.lowrank(u16(A[b]), Q0[b].numpy(), T)
+        rec, orec = U[b] @ RU[b] @ V[b].T, ou @ oru @ ov.T
+        assert rel(rec, orec) <= TOL, f"{tag} b={b}: reconstruction {rel(rec, orec):.2e}"
+        k = r if lead is None else lead
+        assert rel(U[b][:, :k], ou[:, :k]) <= TOL, f"{tag} b={b}: U {rel(U[b][:, :k], ou[:, :k]):.2e}"
+        assert rel(V[b][:, :k], ov[:, :k]) <= TOL, f"{tag} b={b}: V {rel(V[b][:, :k], ov[:, :k]):.2e}"
+        assert rel(RU[b][:k, :k], oru[:k, :k]) <= TOL, f"{tag} b={b}: R_U"
+        assert np.linalg.norm(U[b].T @ U[b] - np.eye(r)) <= 1e-4
+        assert np.linalg.norm(V[b].T @ V[b] - np.eye(r)) <= 1e-4
+        assert np.allclose(np.tril(RU[b], -1), 0)
+    return U, V, RU
+
+
+@pytest.mark.parametrize("r", [1, 4, 8, 16, 24, 32])
+@pytest.mark.parametrize("T", [0, 1, 2])
+def test_small_batch_parity(r, T):
+    batch, m, n = 3, 192, 256
+    A = lowrank_batch(batch, m, n, rank=r + 8, sigma=0.05, seed=r * 7 + T)
+    Q0 = gaussian_q0(batch, n, r, seed=T)
+    check(A, Q0, r, T, tag="small")
+
+
+@pytest.mark.parametrize("m,n,r", [(100, 72, 8), (33, 40, 16), (65, 136, 32), (1, 8, 1), (37, 520, 5)])
+def test_ragged_shapes(m, n, r):
+    if r > m:
+        pytest.skip("r > m")
+    A = lowrank_batch(2, m, n, rank=min(m, n), sigma=0.2, seed=m + n)
+    Q0 = gaussian_q0(2, n, r, seed=1)
+    check(A, Q0, r, 2, tag="ragged")
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_exact_rank_recovery(r):
+    batch, m, n = 2, 256, 384
+    A = exact_rank_batch(batch, m, n, r, seed=r)
+    Q0 = gaussian_q0(batch, n, r, seed=2)
+    say(f"[gpu] exact rank {r}")
+    U, V, RU = run_gpu(A, Q0, r, 2)
+    Af = A.double().numpy()
+    for b in range(batch):
+        assert rel(U[b] @ RU[b] @ V[b].T, Af[b]) <= 1e-4
+
+
+def test_zero_matrix_and_zero_column():
+    batch, m, n, r = 2, 64, 64, 4
+    A = torch.zeros((batch, m, n), dtype=torch.bfloat16)
+    A[1] = lowrank_batch(1, m, n, rank=8, seed=3)[0]
+    Q0 = gaussian_q0(batch, n, r, seed=5)
+    Q0[1, :, 2] = 0.0  # a dropped column of the random sample
+    say("[gpu] zero matrix / zero column")
+    U, V, RU = run_gpu(A, Q0, r, 2)
+    assert not np.any(U[0]) and not np.any(V[0]) and not np.any(RU[0])
+    ou, ov, oru = oracle.lowrank(u16(A[1]), Q0[1].numpy(), 2)
+    assert not np.any(V[1][:, 2]) and not np.any(ov[:, 2])
+    assert rel(U[1] @ RU[1] @ V[1].T, ou @ oru @ ov.T) <= TOL
+
+
+def test_deterministic_and_workspace_independent():
+    batch, m, n, r = 4, 256, 512, 16
+    A = lowrank_batch(batch, m, n, seed=9)
+    Q0 = gaussian_q0(batch, n, r, seed=9)
+    say("[gpu] determinism")
+    a = run_gpu(A, Q0, r, 2)
+    b = run_gpu(A, Q0, r, 2)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_error_paths_write_nothing():
+    batch, m, n, r = 2, 64, 64, 8
+    A = lowrank_batch(batch, m, n, seed=1).to(DEV)
+    Q0 = gaussian_q0(batch, n, r).to(DEV)
+    U = torch.full((batch, m, r), 7.0, device=DEV)
+    V = torch.full((batch, n, r), 7.0, device=DEV)
+    RU = torch.full((batch, r, r), 7.0, device=DEV)
+    need = cfz.cfz_lowrank_workspace_bytes(batch, m, n, r)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    say("[gpu] low-rank error paths")
+    with pytest.raises(cfz.CfzError) as ei:
+        cfz.cfz_lowrank(batch, m, n, r, 2, A, Q0, U, V, RU, ws, need - 256)
+    assert ei.value.status == cfz.CFZ_ERR_WORKSPACE
+    with pytest.raises(cfz.CfzError) as ei:
+        cfz.cfz_lowrank(batch, m, 60, r, 2, A, Q0, U, V, RU, ws)
+    assert ei.value.status == cfz.CFZ_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert bool((U == 7).all()) and bool((V == 7).all()) and bool((RU == 7).all())
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_full_size_layer_batch(r):
+    """57 layers of 1024 x 3072 (rank-16 signal + 0.05 noise) in one call, T = 2;
+    layers 0 and 56 compared at two denoising steps.  At r = 32 the trailing 16
+    columns span noise and are not compared."""
+    batch, m, n, T = 57, 1024, 3072, 2
+    for step in (0, 27):
+        A = lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=1000 + step, device=DEV).cpu()
+        Q0 = gaussian_q0(batch, n, r, seed=2000 + step, device=DEV).cpu()
+        check(A, Q0, r, T, layers=[0, 56], lead=16 if r == 32 else None,
+              tag=f"full r={r} step={step}")
