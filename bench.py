@@ -89,6 +89,78 @@ def cpu_baseline(xs_host, bits, group, budget_s=20.0):
                       f"DELTA), single-threaded C oracle, {t_total:.1f} s"}, np
 
 
+def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps):
+    """All tensors of a step in one compress and one decode launch (rows = tensors x tokens)."""
+    n = rows * cols
+    dev = X.device
+    prev = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    err = torch.empty(n, dtype=torch.float32, device=dev)
+    base = torch.empty(n, dtype=torch.float32, device=dev)
+    codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // group, dtype=torch.float32, device=dev)
+    sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER)
+    rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
+    snd = cfz.cfz_state_create(sd, prev=prev, err=err, x0=X[0])
+    rcv = cfz.cfz_state_create(rd, base=base, x0=X[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
+    for k in range(steps + 1):  # the first step is an untimed warm-up
+        s = 1 + k % (slots - 1)
+        ev[k][0].record()
+        cfz.cfz_compress(snd, X[s], codes, scales)
+        ev[k][1].record()
+        cfz.cfz_decompress(rcv, codes, scales, None)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / steps
+    td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / steps
+    cfz.cfz_state_destroy(snd)
+    cfz.cfz_state_destroy(rcv)
+    bc, bd = algorithmic_bytes(bits, group)
+    return {"workload": f"flux-share all 114 tensors in one launch ({rows}x{cols}), "
+                        f"int{bits} g{group}, delta", "steps": steps,
+            "activation_GB/s": round(2 * n / (tc + td) / 1e9, 2),
+            "compress": {"us": round(tc * 1e6, 2), "GB/s": round(bc * n / tc / 1e9, 1),
+                         "frac_hbm_peak": round(bc * n / tc / 1e9 / HBM_PEAK_GBS, 4)},
+            "decode": {"us": round(td * 1e6, 2), "GB/s": round(bd * n / td / 1e9, 1),
+                       "frac_hbm_peak": round(bd * n / td / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
+    """Algorithm 3 on 57 layer residuals of 1024 x 3072 (rank-16 signal + 0.05 noise)."""
+    from synth import gaussian_q0, lowrank_batch
+
+    A = lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=7, device=dev)
+    out = {"workload": f"{batch} x {m}x{n} bf16, rank-16 + 0.05 noise, T={T}", "per_rank": {}}
+    for r in (8, 16, 32):
+        Q0 = gaussian_q0(batch, n, r, seed=r, device=dev)
+        U = torch.empty(batch, m, r, device=dev)
+        V = torch.empty(batch, n, r, device=dev)
+        RU = torch.empty(batch, r, r, device=dev)
+        ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(batch, m, n, r), dtype=torch.uint8,
+                         device=dev)
+        cfz.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            cfz.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / reps
+        # algorithmic bytes: A read once, Q0 read, U, V, R_U written
+        alg = batch * (2 * m * n + 4 * n * r + 4 * (m + n) * r + 4 * r * r)
+        useful_flop = batch * 2 * m * n * r * (2 * T + 1)
+        out["per_rank"][str(r)] = {
+            "ms_per_call": round(t * 1e3, 4), "us_per_layer": round(t * 1e6 / batch, 2),
+            "achieved_GB/s_single_read": round(alg / t / 1e9, 1),
+            "frac_hbm_peak_single_read": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+            "A_passes": 2 * T + 1,
+            "useful_TFLOP/s": round(useful_flop / t / 1e12, 2),
+            "mfma_TFLOP/s_executed": round(2 * useful_flop / t / 1e12, 2)}
+        del ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--no-batched", action="store_true", help="skip the one-launch-per-step int2 leg")
+    ap.add_argument("--no-lowrank", action="store_true", help="skip the subspace-iteration leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} is not "
@@ -259,6 +333,13 @@ def main():
         },
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
     }
+    if not args.no_batched:
+        print("[bench] batched int2 leg", file=sys.stderr, flush=True)
+        line["batched_int2_g32"] = bench_batched(cfz, torch, X, slots, T * rows, cols, 2, 32,
+                                                 steps=min(K, 10))
+    if not args.no_lowrank:
+        print("[bench] subspace-iteration leg", file=sys.stderr, flush=True)
+        line["lowrank"] = bench_lowrank(cfz, torch, dev)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         sample_tensors = 114
