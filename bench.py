@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--no-batched", action="store_true", help="skip the one-launch-per-step int2 leg")
     ap.add_argument("--no-lowrank", action="store_true", help="skip the subspace-iteration leg")
+    ap.add_argument("--launch", choices=("layer", "tensor", "step"), default="layer",
+                    help="tensors per launch: K+V of a layer (default), one, or the whole step")
+    ap.add_argument("--no-modes", action="store_true", help="skip the other launch granularities")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} is not "
@@ -205,87 +208,118 @@ def main():
     scales = torch.empty((T, n // group), dtype=torch.float32, device=dev)
     sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER)
     rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
-    snd = [cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)]
-    rcv = [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)]
 
-    def compress_phase(slot):
-        for i in range(T):
-            cfz.cfz_compress(snd[i], X[slot, i], codes[i], scales[i])
-
-    def decode_phase():
-        for i in range(T):
-            cfz.cfz_decompress(rcv[i], codes[i], scales[i], None)
+    def fresh_states():
+        s_ = [cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)]
+        r_ = [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)]
+        return s_, r_
 
     def slot_of(step):  # step >= 1; wraps around the pre-generated pool
         return 1 + (step - 1) % (slots - 1)
 
-    graphs = None
-    if not args.no_graph:
-        # capture advances the host-side step counters but enqueues no work; the states are
-        # re-warmed below, so the captured graphs start from step 0 like the eager path
-        print("[bench] capturing HIP graphs", file=sys.stderr, flush=True)
-        graphs = {}
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        dec = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(dec, stream=cap):
-            decode_phase()
-        for s in range(1, slots):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                compress_phase(s)
-            graphs[s] = g
-        graphs["dec"] = dec
+    # tensors per call: 2 = the K and V of one layer, 1 = each tensor alone, T = the whole step
+    per_call = {"layer": 2, "tensor": 1, "step": T}
+
+    def run_mode(mode, K, W, use_graph):
+        g = per_call[mode]
+        calls = [list(range(i, min(i + g, T))) for i in range(0, T, g)]
+        launches = sum((len(c) + 15) // 16 for c in calls)
+        snd, rcv = fresh_states()
+
+        def compress_phase(slot):
+            for c in calls:
+                if len(c) == 1:
+                    cfz.cfz_compress(snd[c[0]], X[slot, c[0]], codes[c[0]], scales[c[0]])
+                else:
+                    cfz.cfz_compress_group([snd[i] for i in c], [X[slot, i] for i in c],
+                                           [codes[i] for i in c], [scales[i] for i in c])
+
+        def decode_phase():
+            for c in calls:
+                if len(c) == 1:
+                    cfz.cfz_decompress(rcv[c[0]], codes[c[0]], scales[c[0]], None)
+                else:
+                    cfz.cfz_decompress_group([rcv[i] for i in c], [codes[i] for i in c],
+                                             [scales[i] for i in c])
+
+        graphs = None
+        if use_graph:
+            # capture advances the host-side step counters but enqueues no work; the states
+            # are re-warmed afterwards, so replays start from step 0 like eager launches
+            graphs = {}
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd, stream=cap):
+                decode_phase()
+            for s_ in range(1, slots):
+                gc = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gc, stream=cap):
+                    compress_phase(s_)
+                graphs[s_] = gc
+            graphs["dec"] = gd
+            torch.cuda.synchronize()
+            for h in snd + rcv:
+                cfz.cfz_state_destroy(h)
+            snd[:], rcv[:] = fresh_states()
+            torch.cuda.synchronize()
+
+        def run_step(step, ev=None):
+            s_ = slot_of(step)
+            if ev is not None:
+                ev[0].record()
+            graphs[s_].replay() if graphs else compress_phase(s_)
+            if ev is not None:
+                ev[1].record()
+            graphs["dec"].replay() if graphs else decode_phase()
+            if ev is not None:
+                ev[2].record()
+
+        for step in range(1, W + 1):
+            run_step(step)
         torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            run_step(W + 1 + k, evs[k])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
         for h in snd + rcv:
             cfz.cfz_state_destroy(h)
-        snd[:] = [cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)]
-        rcv[:] = [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)]
-        torch.cuda.synchronize()
+        t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
+        t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+        return {"elapsed": elapsed, "t_comp": t_comp, "t_dec": t_dec, "launches": launches,
+                "tensors_per_launch": T / launches}
 
-    def run_step(step, ev=None):
-        s = slot_of(step)
-        if ev is not None:
-            ev[0].record()
-        if graphs is not None:
-            graphs[s].replay()
-        else:
-            compress_phase(s)
-        if ev is not None:
-            ev[1].record()
-        if graphs is not None:
-            graphs["dec"].replay()
-        else:
-            decode_phase()
-        if ev is not None:
-            ev[2].record()
-
-    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
-    for step in range(1, W + 1):
-        run_step(step)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        run_step(W + 1 + k, evs[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+    print(f"[bench] timing {K} steps ({args.launch} launches)", file=sys.stderr, flush=True)
+    res = run_mode(args.launch, K, W, not args.no_graph)
+    elapsed, t_comp, t_dec = res["elapsed"], res["t_comp"], res["t_dec"]
     bc, bd = algorithmic_bytes(bits, group)
-    n_launch = K * T
+    n_launch = K * res["launches"]
+    per_launch_elems = n * T / res["launches"]
     avg_comp = t_comp / n_launch
     avg_dec = t_dec / n_launch
-    comp_gbs = bc * n / avg_comp / 1e9
-    dec_gbs = bd * n / avg_dec / 1e9
+    comp_gbs = bc * per_launch_elems / avg_comp / 1e9
+    dec_gbs = bd * per_launch_elems / avg_dec / 1e9
     act_bytes = 2 * n * T * K
     value = act_bytes / elapsed / 1e9
 
-    # achievable copy ceiling on a buffer as large as one step's compress traffic
+    other_modes = {}
+    for mode in ("layer", "tensor", "step"):
+        if mode == args.launch or args.no_modes:
+            continue
+        print(f"[bench] {mode} launches", file=sys.stderr, flush=True)
+        r_ = run_mode(mode, min(K, 10), 1, not args.no_graph)
+        nl = min(K, 10) * r_["launches"]
+        pe = n * T / r_["launches"]
+        other_modes[mode] = {
+            "tensors_per_launch": round(r_["tensors_per_launch"], 2),
+            "activation_GB/s": round(2 * n * T * min(K, 10) / r_["elapsed"] / 1e9, 2),
+            "compress_GB/s": round(bc * pe / (r_["t_comp"] / nl) / 1e9, 1),
+            "decode_GB/s": round(bd * pe / (r_["t_dec"] / nl) / 1e9, 1)}
+
+    # achievable copy ceiling on a buffer as large as two steps of activations
     src = X[1:3].reshape(-1)
     dst = torch.empty_like(src)
     cfz.cfz_stream_copy(src, dst)
@@ -300,7 +334,7 @@ def main():
     del dst
 
     workload = "flux-share-57x2x1024x3072-int4-g64-delta"
-    traffic = load_traffic("compress", workload)
+    traffic = load_traffic("compress", f"{workload}/{args.launch}")
     line = {
         "metric": "codec GB/s of bf16 activation (compress+decode) and % of HBM peak",
         "value": round(value, 2),
@@ -316,13 +350,17 @@ def main():
         "data": "synthetic (seeded AR(1) bf16 activations, alpha 0.98, LogNormal(0,0.5) channel "
                 "scales, 1% outlier channels x20)",
         "config": {"workload": workload, "tensors": T, "rows": rows, "cols": cols, "bits": bits,
-                   "group": group, "ef_mode": "delta", "launch": "one compress and one decode "
-                   "launch per tensor, replayed from HIP graphs" if graphs else
-                   "one compress and one decode launch per tensor, eager"},
+                   "group": group, "ef_mode": "delta",
+                   "launch": {"layer": "one grouped compress and decode launch per layer (K and V)",
+                              "tensor": "one compress and decode launch per tensor",
+                              "step": "grouped launches of 16 tensors over the whole step"}[
+                       args.launch] + (", replayed from HIP graphs" if not args.no_graph else
+                                       ", eager")},
         "roofline": {"bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "cfz_compress_kernel<4,64,DELTA>",
-                     "bytes_per_launch": int(bc * n), "avg_launch_us": round(avg_comp * 1e6, 3)},
+                     "traffic": traffic, "kernel": "cfz_compress_kernel<bits=4, G=64, DELTA>",
+                     "bytes_per_launch": int(bc * per_launch_elems),
+                     "avg_launch_us": round(avg_comp * 1e6, 3)},
         "kernels": {
             "compress": {"avg_launch_us": round(avg_comp * 1e6, 3), "GB/s": round(comp_gbs, 1),
                          "frac_hbm_peak": round(comp_gbs / HBM_PEAK_GBS, 4),
@@ -331,6 +369,7 @@ def main():
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": bd},
             "stream_copy_ceiling_GB/s": round(copy_gbs, 1),
         },
+        "other_launch_granularities": other_modes,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
     }
     if not args.no_batched:
@@ -351,8 +390,6 @@ def main():
         line["cpu_baseline"] = cb
     else:
         line["cpu_baseline"] = None
-    for h in snd + rcv:
-        cfz.cfz_state_destroy(h)
     print(json.dumps(line), flush=True)
 
 

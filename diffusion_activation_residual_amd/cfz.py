@@ -59,6 +59,8 @@ def _load():
         "cfz_scales_bytes": ([C.POINTER(cfz_desc)], sz),
         "cfz_compress": ([p, p, p, p, p], i32),
         "cfz_decompress": ([p, p, p, p, p], i32),
+        "cfz_compress_group": ([i32, p, p, p, p, p], i32),
+        "cfz_decompress_group": ([i32, p, p, p, p, p], i32),
         "cfz_lowrank_workspace_bytes": ([i64, i64, i64, i32], sz),
         "cfz_lowrank": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, sz, p], i32),
         "cfz_stream_copy": ([p, p, sz, p], i32),
@@ -174,6 +176,33 @@ def cfz_compress(handle, x, codes, scales, stream=None) -> None:
 def cfz_decompress(handle, codes, scales, xhat=None, stream=None) -> None:
     _check(_lib.cfz_decompress(handle, _ptr(codes), _ptr(scales), _bf16_ptr(xhat),
                                _stream(stream)), "cfz_decompress")
+
+
+def _ptr_array(items, fn=_ptr):
+    arr = (C.c_void_p * max(len(items), 1))()
+    for i, t in enumerate(items):
+        arr[i] = fn(t)
+    return arr
+
+
+def cfz_compress_group(handles, xs, codes, scales, stream=None) -> None:
+    """One grouped compress over len(handles) tensors (entry i: handles[i], xs[i], ...)."""
+    n = len(handles)
+    if not (len(xs) == len(codes) == len(scales) == n):
+        raise ValueError("all lists must have one entry per state")
+    _check(_lib.cfz_compress_group(n, _ptr_array(handles, lambda h: h), _ptr_array(xs, _bf16_ptr),
+                                   _ptr_array(codes), _ptr_array(scales), _stream(stream)),
+           "cfz_compress_group")
+
+
+def cfz_decompress_group(handles, codes, scales, xhats=None, stream=None) -> None:
+    n = len(handles)
+    if not (len(codes) == len(scales) == n) or (xhats is not None and len(xhats) != n):
+        raise ValueError("all lists must have one entry per state")
+    xa = None if xhats is None else _ptr_array(xhats, _bf16_ptr)
+    _check(_lib.cfz_decompress_group(n, _ptr_array(handles, lambda h: h), _ptr_array(codes),
+                                     _ptr_array(scales), xa, _stream(stream)),
+           "cfz_decompress_group")
 
 
 def cfz_lowrank_workspace_bytes(batch, m, n, r) -> int:

@@ -29,6 +29,14 @@ cfz_status fail(cfz_status st, const char *fmt, ...)
     return st;
 }
 
+// Re-labels the current error text with the group entry it came from.
+cfz_status fail_entry(cfz_status st, int32_t i)
+{
+    char detail[sizeof g_last_error];
+    memcpy(detail, g_last_error, sizeof detail);
+    return fail(st, "entry %d: %s", i, detail);
+}
+
 cfz_status hip_fail(hipError_t e, const char *what)
 {
     return fail(CFZ_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -207,8 +215,9 @@ int64_t cfz_state_steps(const cfz_state *s)
     return s->steps;
 }
 
-cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *scales,
-                        void *stream)
+// Per-tensor checks shared by the single and grouped entry points.
+static cfz_status check_compress_one(cfz_state *s, const uint16_t *x, uint8_t *codes, float *scales,
+                                     cfz::CompressItem *item)
 {
     cfz_status st = check_state(s);
     if (st != CFZ_OK)
@@ -221,17 +230,13 @@ cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *
         return fail(CFZ_ERR_NULL, "x, codes and scales are required");
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
         return fail(CFZ_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
-    cfz::CompressArgs a{x, s->bufs.prev_bf16, s->bufs.base_f32, s->bufs.err_f32, codes, scales,
-                        n / 8, d.bits, d.group, d.ef_mode};
-    hipError_t e = cfz::launch_compress(a, (hipStream_t)stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "compress launch");
-    ++s->steps;
+    *item = cfz::CompressItem{x, s->bufs.prev_bf16, s->bufs.base_f32, s->bufs.err_f32, codes,
+                              scales, n};
     return CFZ_OK;
 }
 
-cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scales,
-                          uint16_t *xhat, void *stream)
+static cfz_status check_decode_one(cfz_state *s, const uint8_t *codes, const float *scales,
+                                   uint16_t *xhat, cfz::DecodeItem *item)
 {
     cfz_status st = check_state(s);
     if (st != CFZ_OK)
@@ -244,18 +249,125 @@ cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scale
         return fail(CFZ_ERR_NULL, "codes and scales are required");
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(xhat))
         return fail(CFZ_ERR_ALIGN, "codes, scales and xhat must be 16-byte aligned");
-    cfz::DecodeArgs a{codes, scales, s->bufs.base_f32, xhat, n / 8, d.bits, d.group};
-    hipError_t e = cfz::launch_decode(a, (hipStream_t)stream);
+    *item = cfz::DecodeItem{codes, scales, s->bufs.base_f32, xhat, n};
+    return CFZ_OK;
+}
+
+static bool same_codec(const cfz_desc &a, const cfz_desc &b)
+{
+    return a.bits == b.bits && a.group == b.group && a.ef_mode == b.ef_mode && a.role == b.role;
+}
+
+cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *scales,
+                        void *stream)
+{
+    cfz::CompressItem item;
+    cfz_status st = check_compress_one(s, x, codes, scales, &item);
+    if (st != CFZ_OK)
+        return st;
+    const cfz_desc &d = s->desc;
+    hipError_t e = cfz::launch_compress(&item, 1, d.bits, d.group, d.ef_mode, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "compress launch");
+    ++s->steps;
+    return CFZ_OK;
+}
+
+cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scales,
+                          uint16_t *xhat, void *stream)
+{
+    cfz::DecodeItem item;
+    cfz_status st = check_decode_one(s, codes, scales, xhat, &item);
+    if (st != CFZ_OK)
+        return st;
+    const cfz_desc &d = s->desc;
+    hipError_t e = cfz::launch_decode(&item, 1, d.bits, d.group, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");
     ++s->steps;
     return CFZ_OK;
 }
 
+// Group checks common to both directions: array presence, one codec setting, no repeats.
+static cfz_status check_group(int32_t count, cfz_state *const *states, const void *a, const void *b,
+                              const void *c)
+{
+    if (count < 0)
+        return fail(CFZ_ERR_SHAPE, "count = %d", count);
+    if (count == 0)
+        return CFZ_OK;
+    if (!states || !a || !b || !c)
+        return fail(CFZ_ERR_NULL, "state and buffer arrays are required");
+    for (int32_t i = 0; i < count; ++i) {
+        cfz_status st = check_state(states[i]);
+        if (st != CFZ_OK)
+            return fail_entry(st, i);
+        if (!same_codec(states[i]->desc, states[0]->desc))
+            return fail(CFZ_ERR_MODE, "entry %d: bits, group, mode and role must match entry 0", i);
+        for (int32_t j = 0; j < i; ++j)
+            if (states[j] == states[i])
+                return fail(CFZ_ERR_MODE, "entries %d and %d are the same state", j, i);
+    }
+    return CFZ_OK;
+}
+
+cfz_status cfz_compress_group(int32_t count, cfz_state *const *senders, const uint16_t *const *xs,
+                              uint8_t *const *codes, float *const *scales, void *stream)
+{
+    cfz_status st = check_group(count, senders, xs, codes, scales);
+    if (st != CFZ_OK || count == 0)
+        return st;
+    cfz::CompressItem *items = new (std::nothrow) cfz::CompressItem[count];
+    if (!items)
+        return fail(CFZ_ERR_NULL, "out of host memory");
+    for (int32_t i = 0; i < count && st == CFZ_OK; ++i)
+        if ((st = check_compress_one(senders[i], xs[i], codes[i], scales[i], &items[i])) != CFZ_OK)
+            st = fail_entry(st, i);
+    if (st == CFZ_OK) {
+        const cfz_desc &d = senders[0]->desc;
+        hipError_t e = cfz::launch_compress(items, count, d.bits, d.group, d.ef_mode,
+                                            (hipStream_t)stream);
+        if (e != hipSuccess)
+            st = hip_fail(e, "grouped compress launch");
+        else
+            for (int32_t i = 0; i < count; ++i)
+                ++senders[i]->steps;
+    }
+    delete[] items;
+    return st;
+}
+
+cfz_status cfz_decompress_group(int32_t count, cfz_state *const *receivers,
+                                const uint8_t *const *codes, const float *const *scales,
+                                uint16_t *const *xhat, void *stream)
+{
+    cfz_status st = check_group(count, receivers, codes, scales, codes);
+    if (st != CFZ_OK || count == 0)
+        return st;
+    cfz::DecodeItem *items = new (std::nothrow) cfz::DecodeItem[count];
+    if (!items)
+        return fail(CFZ_ERR_NULL, "out of host memory");
+    for (int32_t i = 0; i < count && st == CFZ_OK; ++i)
+        if ((st = check_decode_one(receivers[i], codes[i], scales[i], xhat ? xhat[i] : nullptr,
+                                   &items[i])) != CFZ_OK)
+            st = fail_entry(st, i);
+    if (st == CFZ_OK) {
+        const cfz_desc &d = receivers[0]->desc;
+        hipError_t e = cfz::launch_decode(items, count, d.bits, d.group, (hipStream_t)stream);
+        if (e != hipSuccess)
+            st = hip_fail(e, "grouped decode launch");
+        else
+            for (int32_t i = 0; i < count; ++i)
+                ++receivers[i]->steps;
+    }
+    delete[] items;
+    return st;
+}
+
 size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r)
 {
     if (batch < 0 || m <= 0 || n <= 0 || r < 1 || r > 32 || r > m || r > n || n % 8 != 0 ||
-        m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
+        m > (1 << 20) || n > (1 << 20) || batch > (1 << 20) || m * n > ((int64_t)1 << 30))
         return 0;
     return cfz::lowrank_workspace_bytes(batch, m, n, r);
 }
@@ -273,6 +385,8 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
         return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
     if (n % 8 != 0)
         return fail(CFZ_ERR_SHAPE, "n = %lld must be a multiple of 8 (16-byte rows)", (long long)n);
+    if (m * n > ((int64_t)1 << 30))
+        return fail(CFZ_ERR_SHAPE, "m * n = %lld exceeds 2^30 elements per matrix", (long long)(m * n));
     if (m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
         return fail(CFZ_ERR_SHAPE, "sizes too large");
     if (batch == 0)

@@ -9,28 +9,30 @@ namespace cfz {
 
 enum { kDelta = 0, kLiteral = 1, kOff = 2 };
 
-struct CompressArgs {
+constexpr int kMaxGroup = 16;  // tensors per codec launch
+
+struct CompressItem {
     const uint16_t *x;
     uint16_t *prev;
     float *base;
     float *err;
     uint8_t *codes;
     float *scales;
-    int64_t nchunks;  // elements / 8
-    int bits, group, mode;
+    int64_t n;  // elements, a multiple of the group size
 };
 
-struct DecodeArgs {
+struct DecodeItem {
     const uint8_t *codes;
     const float *scales;
     float *base;
     uint16_t *xhat;  // may be null
-    int64_t nchunks;
-    int bits, group;
+    int64_t n;
 };
 
-hipError_t launch_compress(const CompressArgs &a, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+// Any count: tensors are launched kMaxGroup at a time; empty tensors are skipped.
+hipError_t launch_compress(const CompressItem *items, int count, int bits, int group, int mode,
+                           hipStream_t st);
+hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, hipStream_t st);
 hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, float *base, float *err,
                          int64_t nchunks, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t nvec, hipStream_t st);

@@ -7,13 +7,20 @@
 // Splits").  The quantizer is group-wise symmetric absmax, low-bit
 // (4 and 2 bit), fp32 scales, round to nearest even.
 //
-// Layout of the work: the tensor is a flat array of N = rows*cols elements
+// Layout of the work: a tensor is a flat array of N = rows*cols elements
 // (groups never straddle rows because cols % group == 0).  One lane owns a
-// chunk of 8 consecutive elements: a 16-byte bf16 load, 32 bytes of fp32
-// state, and exactly one packed code word (32 bits at 4 bit, 16 bits at 2 bit).
-// A group of G elements is G/8 adjacent lanes of one wavefront, so its absmax
-// is a DPP butterfly inside a row of 16 lanes -- no LDS, no barrier.
-// Every kernel is a pure stream: each element is read once and written once.
+// quad of 4 consecutive elements: an 8-byte bf16 load, 16 bytes of fp32 state
+// and one packed code field of 16 bits (int4) or 8 bits (int2).  Every load and
+// store instruction of a wavefront therefore covers one contiguous span, which
+// is what keeps the mixed read/write stream near the copy ceiling.  A group of
+// G elements is G/4 adjacent lanes, so its absmax is a DPP butterfly inside a
+// row of 16 lanes (plus one swizzle across rows for G = 128) -- no LDS, no
+// barrier.  Every kernel is a pure stream: each byte is read or written once.
+//
+// One launch may cover up to kMaxGroup separately allocated tensors of the same
+// bits/group/mode: a small table in the kernel arguments maps work-group ranges
+// to tensors, so the K and V of a layer (or any set of tensors available at
+// once) cost one launch ramp instead of several.
 //
 // Bit-exactness: fp32 IEEE division for the scale and for r/s, rint (ties to
 // even), and explicit fma for the error and base updates; the library is
@@ -38,7 +45,7 @@ __device__ __forceinline__ void st_nt(u32x4 v, u32x4 *p) { __builtin_nontemporal
 __device__ __forceinline__ void st_nt(f32x4 v, f32x4 *p) { __builtin_nontemporal_store(v, p); }
 
 // element k (0..7) of 8 bf16 values held in a u32x4, widened to fp32 exactly
-__device__ __forceinline__ float bf16_at(const u32x4 &v, int k)
+__device__ __forceinline__ float bf16_at8(const u32x4 &v, int k)
 {
     uint32_t w = v[k >> 1];
     return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -50,7 +57,7 @@ __device__ __forceinline__ float dpp_f32(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// max over the LANES adjacent lanes that hold one group (LANES = G/8, a power of two <= 16)
+// max over LANES adjacent lanes (a power of two <= 16), inside one row of 16 lanes
 template <int LANES>
 __device__ __forceinline__ float group_max(float v)
 {
@@ -69,164 +76,212 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// ---------------------------------------------------------------- tensor tables
+
+template <int MAXT>
+struct CompressTable {
+    int32_t count;
+    int32_t begin[MAXT + 1];  // first work-group of each tensor; begin[count] = grid size
+    int64_t nquads[MAXT];
+    const uint16_t *x[MAXT];
+    uint16_t *prev[MAXT];
+    float *base[MAXT];
+    float *err[MAXT];
+    uint8_t *codes[MAXT];
+    float *scales[MAXT];
+};
+
+template <int MAXT>
+struct DecodeTable {
+    int32_t count;
+    int32_t begin[MAXT + 1];
+    int64_t nquads[MAXT];
+    const uint8_t *codes[MAXT];
+    const float *scales[MAXT];
+    float *base[MAXT];
+    uint16_t *xhat[MAXT];
+};
+
+// the tensor a work-group belongs to (uniform, evaluated in scalar registers)
+template <int MAXT>
+__device__ __forceinline__ int find_tensor(const int32_t *begin, int count)
+{
+    int t = 0;
+#pragma unroll
+    for (int i = 1; i < MAXT; ++i)
+        if (i < count && (int)blockIdx.x >= begin[i])
+            t = i;
+    return t;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 ld_nt(const u32x2 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(u32x2 v, u32x2 *p) { __builtin_nontemporal_store(v, p); }
+
+// element k (0..3) of 4 bf16 values held in a u32x2, widened to fp32 exactly
+__device__ __forceinline__ float bf16_at(const u32x2 &v, int k)
+{
+    uint32_t w = v[k >> 1];
+    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// lane ^ 16 inside each half of the wavefront (ds_swizzle bit mode: and 0x1f, xor 0x10)
+__device__ __forceinline__ float swizzle_xor16(float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401f));
+}
+
+// max over the LANES adjacent lanes of one group (LANES = G/4, a power of two <= 32)
+template <int LANES>
+__device__ __forceinline__ float group_max4(float v)
+{
+    v = group_max<(LANES < 16 ? LANES : 16)>(v);
+    if constexpr (LANES >= 32) v = fmaxf(v, swizzle_xor16(v));
+    return v;
+}
+
 // ---------------------------------------------------------------- compress
 
-// One chunk of 8 elements per lane per unrolled slot; UNROLL slots per lane,
-// strided by the block size so that every load instruction is fully coalesced.
-template <int BITS, int G, int MODE, int UNROLL>
-__global__ void __launch_bounds__(kBlock)
-cfz_compress_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ prev,
-                    float *__restrict__ base, float *__restrict__ err,
-                    uint8_t *__restrict__ codes, float *__restrict__ scales, int64_t nchunks)
+template <int BITS, int G, int MODE, int UNROLL, int MAXT>
+__global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTable<MAXT> tab)
 {
-    constexpr int LANES = G / 8;
+    constexpr int LANES = G / 4;
     constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
     constexpr uint32_t MASK = (1u << BITS) - 1u;
     constexpr bool USE_PREV = (MODE == kDelta);
     constexpr bool USE_BASE = (MODE == kLiteral || MODE == kOff);
     constexpr bool USE_ERR = (MODE == kDelta || MODE == kLiteral);
 
-    const int64_t c0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
+    const int t = find_tensor<MAXT>(tab.begin, tab.count);
+    const int64_t nq = tab.nquads[t];
+    const uint16_t *__restrict__ x = tab.x[t];
+    uint16_t *__restrict__ prev = tab.prev[t];
+    float *__restrict__ base = tab.base[t];
+    float *__restrict__ err = tab.err[t];
+    uint8_t *__restrict__ codes = tab.codes[t];
+    float *__restrict__ scales = tab.scales[t];
+    const int64_t q0 = (int64_t)((int)blockIdx.x - tab.begin[t]) * (kBlock * UNROLL) + threadIdx.x;
 
-    u32x4 xv[UNROLL], pv[UNROLL];
-    f32x4 s0[UNROLL], s1[UNROLL], e0[UNROLL], e1[UNROLL];
-
+    u32x2 xv[UNROLL], pv[UNROLL];
+    f32x4 sv[UNROLL], ev[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-        const int64_t c = c0 + (int64_t)u * kBlock;
-        const bool live = c < nchunks;
-        xv[u] = live ? ld_nt((const u32x4 *)(x + 8 * c)) : u32x4{0, 0, 0, 0};
+        const int64_t q = q0 + (int64_t)u * kBlock;
+        const bool live = q < nq;
+        xv[u] = live ? ld_nt((const u32x2 *)(x + 4 * q)) : u32x2{0, 0};
         if constexpr (USE_PREV)
-            pv[u] = live ? ld_nt((const u32x4 *)(prev + 8 * c)) : u32x4{0, 0, 0, 0};
-        if constexpr (USE_BASE) {
-            s0[u] = live ? ld_nt((const f32x4 *)(base + 8 * c)) : f32x4{0, 0, 0, 0};
-            s1[u] = live ? ld_nt((const f32x4 *)(base + 8 * c + 4)) : f32x4{0, 0, 0, 0};
-        }
-        if constexpr (USE_ERR) {
-            e0[u] = live ? ld_nt((const f32x4 *)(err + 8 * c)) : f32x4{0, 0, 0, 0};
-            e1[u] = live ? ld_nt((const f32x4 *)(err + 8 * c + 4)) : f32x4{0, 0, 0, 0};
-        }
+            pv[u] = live ? ld_nt((const u32x2 *)(prev + 4 * q)) : u32x2{0, 0};
+        if constexpr (USE_BASE)
+            sv[u] = live ? ld_nt((const f32x4 *)(base + 4 * q)) : f32x4{0, 0, 0, 0};
+        if constexpr (USE_ERR)
+            ev[u] = live ? ld_nt((const f32x4 *)(err + 4 * q)) : f32x4{0, 0, 0, 0};
     }
 
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-        const int64_t c = c0 + (int64_t)u * kBlock;
-        const bool live = c < nchunks;
+        const int64_t q = q0 + (int64_t)u * kBlock;
+        const bool live = q < nq;
 
-        float r[8];
+        float r[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
             const float xk = bf16_at(xv[u], k);
             if constexpr (MODE == kDelta)
-                r[k] = (xk - bf16_at(pv[u], k)) + (k < 4 ? e0[u][k] : e1[u][k - 4]);
+                r[k] = (xk - bf16_at(pv[u], k)) + ev[u][k];
             else if constexpr (MODE == kLiteral)
-                r[k] = (xk - (k < 4 ? s0[u][k] : s1[u][k - 4])) + (k < 4 ? e0[u][k] : e1[u][k - 4]);
+                r[k] = (xk - sv[u][k]) + ev[u][k];
             else
-                r[k] = xk - (k < 4 ? s0[u][k] : s1[u][k - 4]);
+                r[k] = xk - sv[u][k];
         }
 
-        float a = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            a = fmaxf(a, fabsf(r[k]));
-        a = group_max<LANES>(a);
+        float a = fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3])));
+        a = group_max4<LANES>(a);
         const float s = a / QMAX;        // IEEE fp32 division
         const bool zero = (s == 0.0f);
 
         uint32_t word = 0;
-        float qf[8];
+        float qf[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            float t = __builtin_rintf(r[k] / s);   // IEEE division, ties to even
-            t = fminf(fmaxf(t, -QMAX), QMAX);
-            t = zero ? 0.0f : t;
-            qf[k] = t;
-            word |= ((uint32_t)(int)t & MASK) << (BITS * k);
+        for (int k = 0; k < 4; ++k) {
+            float v = __builtin_rintf(r[k] / s);   // IEEE division, ties to even
+            v = fminf(fmaxf(v, -QMAX), QMAX);
+            v = zero ? 0.0f : v;
+            qf[k] = v;
+            word |= ((uint32_t)(int)v & MASK) << (BITS * k);
         }
 
         if (!live)
             continue;
         if constexpr (BITS == 4)
-            ((uint32_t *)codes)[c] = word;
+            __builtin_nontemporal_store((uint16_t)word, (uint16_t *)codes + q);
         else
-            ((uint16_t *)codes)[c] = (uint16_t)word;
+            __builtin_nontemporal_store((uint8_t)word, codes + q);
         if ((threadIdx.x & (LANES - 1)) == 0)
-            scales[c / LANES] = s;
-
+            scales[q / LANES] = s;
         if constexpr (USE_ERR) {
-            f32x4 n0, n1;
+            f32x4 n;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                n0[k] = __builtin_fmaf(-qf[k], s, r[k]);
-                n1[k] = __builtin_fmaf(-qf[k + 4], s, r[k + 4]);
-            }
-            st_nt(n0, (f32x4 *)(err + 8 * c));
-            st_nt(n1, (f32x4 *)(err + 8 * c + 4));
+            for (int k = 0; k < 4; ++k)
+                n[k] = __builtin_fmaf(-qf[k], s, r[k]);
+            st_nt(n, (f32x4 *)(err + 4 * q));
         }
         if constexpr (USE_PREV)
-            st_nt(xv[u], (u32x4 *)(prev + 8 * c));
+            st_nt(xv[u], (u32x2 *)(prev + 4 * q));
         if constexpr (USE_BASE) {
-            f32x4 n0 = s0[u], n1 = s1[u];
+            f32x4 n = sv[u];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (qf[k] != 0.0f) n0[k] = __builtin_fmaf(qf[k], s, n0[k]);
-                if (qf[k + 4] != 0.0f) n1[k] = __builtin_fmaf(qf[k + 4], s, n1[k]);
-            }
-            st_nt(n0, (f32x4 *)(base + 8 * c));
-            st_nt(n1, (f32x4 *)(base + 8 * c + 4));
+            for (int k = 0; k < 4; ++k)
+                if (qf[k] != 0.0f)
+                    n[k] = __builtin_fmaf(qf[k], s, n[k]);
+            st_nt(n, (f32x4 *)(base + 4 * q));
         }
     }
 }
 
 // ---------------------------------------------------------------- decode
 
-template <int BITS, int G, bool XHAT, int UNROLL>
-__global__ void __launch_bounds__(kBlock)
-cfz_decode_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
-                  float *__restrict__ base, uint16_t *__restrict__ xhat, int64_t nchunks)
+template <int BITS, int G, int UNROLL, int MAXT>
+__global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MAXT> tab)
 {
-    constexpr int LANES = G / 8;
-    const int64_t c0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
+    constexpr int LANES = G / 4;
+    const int t = find_tensor<MAXT>(tab.begin, tab.count);
+    const int64_t nq = tab.nquads[t];
+    const uint8_t *__restrict__ codes = tab.codes[t];
+    const float *__restrict__ scales = tab.scales[t];
+    float *__restrict__ base = tab.base[t];
+    uint16_t *__restrict__ xhat = tab.xhat[t];
+    const int64_t q0 = (int64_t)((int)blockIdx.x - tab.begin[t]) * (kBlock * UNROLL) + threadIdx.x;
 
     uint32_t word[UNROLL];
     float sc[UNROLL];
-    f32x4 b0[UNROLL], b1[UNROLL];
+    f32x4 bv[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-        const int64_t c = c0 + (int64_t)u * kBlock;
-        const bool live = c < nchunks;
+        const int64_t q = q0 + (int64_t)u * kBlock;
+        const bool live = q < nq;
         if constexpr (BITS == 4)
-            word[u] = live ? __builtin_nontemporal_load((const uint32_t *)codes + c) : 0u;
+            word[u] = live ? (uint32_t)__builtin_nontemporal_load((const uint16_t *)codes + q) : 0u;
         else
-            word[u] = live ? (uint32_t)__builtin_nontemporal_load((const uint16_t *)codes + c) : 0u;
-        sc[u] = live ? scales[c / LANES] : 0.0f;
-        b0[u] = live ? ld_nt((const f32x4 *)(base + 8 * c)) : f32x4{0, 0, 0, 0};
-        b1[u] = live ? ld_nt((const f32x4 *)(base + 8 * c + 4)) : f32x4{0, 0, 0, 0};
+            word[u] = live ? (uint32_t)__builtin_nontemporal_load(codes + q) : 0u;
+        sc[u] = live ? scales[q / LANES] : 0.0f;
+        bv[u] = live ? ld_nt((const f32x4 *)(base + 4 * q)) : f32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-        const int64_t c = c0 + (int64_t)u * kBlock;
-        if (c >= nchunks)
+        const int64_t q = q0 + (int64_t)u * kBlock;
+        if (q >= nq)
             continue;
-        float b[8];
+        f32x4 b = bv[u];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            b[k] = b0[u][k];
-            b[k + 4] = b1[u][k];
+            const int c = __builtin_amdgcn_sbfe(word[u], BITS * k, BITS);  // sign-extended field
+            if (c != 0)
+                b[k] = __builtin_fmaf((float)c, sc[u], b[k]);
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int q = __builtin_amdgcn_sbfe(word[u], BITS * k, BITS);  // sign-extended field
-            if (q != 0)
-                b[k] = __builtin_fmaf((float)q, sc[u], b[k]);
-        }
-        st_nt(f32x4{b[0], b[1], b[2], b[3]}, (f32x4 *)(base + 8 * c));
-        st_nt(f32x4{b[4], b[5], b[6], b[7]}, (f32x4 *)(base + 8 * c + 4));
-        if constexpr (XHAT) {
-            u32x4 h = {pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
-                       pack_bf16x2(b[6], b[7])};
-            st_nt(h, (u32x4 *)(xhat + 8 * c));
-        }
+        st_nt(b, (f32x4 *)(base + 4 * q));
+        if (xhat)
+            st_nt(u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])}, (u32x2 *)(xhat + 4 * q));
     }
 }
 
@@ -247,8 +302,8 @@ cfz_warmup_kernel(const uint16_t *__restrict__ x0, uint16_t *__restrict__ prev,
         f32x4 b0, b1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            b0[k] = bf16_at(xv, k);
-            b1[k] = bf16_at(xv, k + 4);
+            b0[k] = bf16_at8(xv, k);
+            b1[k] = bf16_at8(xv, k + 4);
         }
         *(f32x4 *)(base + 8 * c) = b0;
         *(f32x4 *)(base + 8 * c + 4) = b1;
@@ -288,76 +343,168 @@ static inline unsigned grid_for(int64_t items, int64_t per_block)
     return (unsigned)((items + per_block - 1) / per_block);
 }
 
+// Launches over fewer quads than this ramp up too briefly for one quad per lane
+// to keep enough bytes in flight; they take four quads per lane instead.
+constexpr int64_t kBigLaunchQuads = (int64_t)4 << 20;
+
+template <int MAXT, typename Table>
+static bool fill_begin(Table &tab, const int64_t *nq, int count, int64_t per_block)
+{
+    tab.count = count;
+    int64_t acc = 0;
+    for (int i = 0; i < count; ++i) {
+        tab.begin[i] = (int32_t)acc;
+        tab.nquads[i] = nq[i];
+        acc += (nq[i] + per_block - 1) / per_block;
+        if (acc > INT32_MAX)
+            return false;
+    }
+    for (int i = count; i <= MAXT; ++i)
+        tab.begin[i] = (int32_t)acc;
+    for (int i = count; i < MAXT; ++i)
+        tab.nquads[i] = 0;
+    return true;
+}
+
+template <int BITS, int G, int MODE, int UNROLL, int MAXT>
+static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t st)
+{
+    CompressTable<MAXT> tab{};
+    int64_t nq[MAXT];
+    for (int i = 0; i < count; ++i) {
+        nq[i] = it[i].n / 4;
+        tab.x[i] = it[i].x;
+        tab.prev[i] = it[i].prev;
+        tab.base[i] = it[i].base;
+        tab.err[i] = it[i].err;
+        tab.codes[i] = it[i].codes;
+        tab.scales[i] = it[i].scales;
+    }
+    if (!fill_begin<MAXT>(tab, nq, count, (int64_t)kBlock * UNROLL))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, UNROLL, MAXT>), dim3(tab.begin[count]),
+                       dim3(kBlock), 0, st, tab);
+    return hipGetLastError();
+}
+
 template <int BITS, int G, int MODE>
-static hipError_t launch_compress_t(const CompressArgs &a, hipStream_t st)
+static hipError_t compress_g(const CompressItem *it, int count, int64_t total_quads, hipStream_t st)
 {
-    constexpr int UNROLL = 2;
-    const unsigned grid = grid_for(a.nchunks, (int64_t)kBlock * UNROLL);
-    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, UNROLL>), dim3(grid), dim3(kBlock), 0,
-                       st, a.x, a.prev, a.base, a.err, a.codes, a.scales, a.nchunks);
-    return hipGetLastError();
+    const bool big = total_quads >= kBigLaunchQuads;
+    if (count == 1)
+        return big ? compress_chunk<BITS, G, MODE, 1, 1>(it, 1, st)
+                   : compress_chunk<BITS, G, MODE, 4, 1>(it, 1, st);
+    return big ? compress_chunk<BITS, G, MODE, 1, kMaxGroup>(it, count, st)
+               : compress_chunk<BITS, G, MODE, 4, kMaxGroup>(it, count, st);
 }
 
 template <int BITS, int G>
-static hipError_t launch_compress_g(const CompressArgs &a, hipStream_t st)
+static hipError_t compress_m(const CompressItem *it, int count, int mode, int64_t tq, hipStream_t st)
 {
-    switch (a.mode) {
-    case kDelta: return launch_compress_t<BITS, G, kDelta>(a, st);
-    case kLiteral: return launch_compress_t<BITS, G, kLiteral>(a, st);
-    default: return launch_compress_t<BITS, G, kOff>(a, st);
+    switch (mode) {
+    case kDelta: return compress_g<BITS, G, kDelta>(it, count, tq, st);
+    case kLiteral: return compress_g<BITS, G, kLiteral>(it, count, tq, st);
+    default: return compress_g<BITS, G, kOff>(it, count, tq, st);
     }
 }
 
 template <int BITS>
-static hipError_t launch_compress_b(const CompressArgs &a, hipStream_t st)
+static hipError_t compress_b(const CompressItem *it, int count, int group, int mode, int64_t tq,
+                             hipStream_t st)
 {
-    switch (a.group) {
-    case 8: return launch_compress_g<BITS, 8>(a, st);
-    case 16: return launch_compress_g<BITS, 16>(a, st);
-    case 32: return launch_compress_g<BITS, 32>(a, st);
-    case 64: return launch_compress_g<BITS, 64>(a, st);
-    default: return launch_compress_g<BITS, 128>(a, st);
+    switch (group) {
+    case 8: return compress_m<BITS, 8>(it, count, mode, tq, st);
+    case 16: return compress_m<BITS, 16>(it, count, mode, tq, st);
+    case 32: return compress_m<BITS, 32>(it, count, mode, tq, st);
+    case 64: return compress_m<BITS, 64>(it, count, mode, tq, st);
+    default: return compress_m<BITS, 128>(it, count, mode, tq, st);
     }
 }
 
-hipError_t launch_compress(const CompressArgs &a, hipStream_t st)
+hipError_t launch_compress(const CompressItem *items, int count, int bits, int group, int mode,
+                           hipStream_t st)
 {
-    if (a.nchunks == 0)
-        return hipSuccess;
-    return a.bits == 4 ? launch_compress_b<4>(a, st) : launch_compress_b<2>(a, st);
+    CompressItem chunk[kMaxGroup];
+    int k = 0;
+    int64_t tq = 0;
+    for (int i = 0; i <= count; ++i) {
+        if (i < count && items[i].n > 0) {
+            chunk[k++] = items[i];
+            tq += items[i].n / 4;
+        }
+        if ((k == kMaxGroup || i == count) && k > 0) {
+            hipError_t e = bits == 4 ? compress_b<4>(chunk, k, group, mode, tq, st)
+                                     : compress_b<2>(chunk, k, group, mode, tq, st);
+            if (e != hipSuccess)
+                return e;
+            k = 0;
+            tq = 0;
+        }
+    }
+    return hipSuccess;
 }
 
-template <int BITS, int G>
-static hipError_t launch_decode_g(const DecodeArgs &a, hipStream_t st)
+template <int BITS, int G, int UNROLL, int MAXT>
+static hipError_t decode_chunk(const DecodeItem *it, int count, hipStream_t st)
 {
-    constexpr int UNROLL = 2;
-    const unsigned grid = grid_for(a.nchunks, (int64_t)kBlock * UNROLL);
-    if (a.xhat)
-        hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, true, UNROLL>), dim3(grid), dim3(kBlock), 0,
-                           st, a.codes, a.scales, a.base, a.xhat, a.nchunks);
-    else
-        hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, false, UNROLL>), dim3(grid), dim3(kBlock),
-                           0, st, a.codes, a.scales, a.base, a.xhat, a.nchunks);
+    DecodeTable<MAXT> tab{};
+    int64_t nq[MAXT];
+    for (int i = 0; i < count; ++i) {
+        nq[i] = it[i].n / 4;
+        tab.codes[i] = it[i].codes;
+        tab.scales[i] = it[i].scales;
+        tab.base[i] = it[i].base;
+        tab.xhat[i] = it[i].xhat;
+    }
+    if (!fill_begin<MAXT>(tab, nq, count, (int64_t)kBlock * UNROLL))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, UNROLL, MAXT>), dim3(tab.begin[count]),
+                       dim3(kBlock), 0, st, tab);
     return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st)
+template <int BITS, int G>
+static hipError_t decode_g(const DecodeItem *it, int count, int64_t tq, hipStream_t st)
 {
-    switch (a.group) {
-    case 8: return launch_decode_g<BITS, 8>(a, st);
-    case 16: return launch_decode_g<BITS, 16>(a, st);
-    case 32: return launch_decode_g<BITS, 32>(a, st);
-    case 64: return launch_decode_g<BITS, 64>(a, st);
-    default: return launch_decode_g<BITS, 128>(a, st);
+    const bool big = tq >= kBigLaunchQuads;
+    if (count == 1)
+        return big ? decode_chunk<BITS, G, 1, 1>(it, 1, st) : decode_chunk<BITS, G, 4, 1>(it, 1, st);
+    return big ? decode_chunk<BITS, G, 1, kMaxGroup>(it, count, st)
+               : decode_chunk<BITS, G, 4, kMaxGroup>(it, count, st);
+}
+
+template <int BITS>
+static hipError_t decode_b(const DecodeItem *it, int count, int group, int64_t tq, hipStream_t st)
+{
+    switch (group) {
+    case 8: return decode_g<BITS, 8>(it, count, tq, st);
+    case 16: return decode_g<BITS, 16>(it, count, tq, st);
+    case 32: return decode_g<BITS, 32>(it, count, tq, st);
+    case 64: return decode_g<BITS, 64>(it, count, tq, st);
+    default: return decode_g<BITS, 128>(it, count, tq, st);
     }
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t st)
+hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, hipStream_t st)
 {
-    if (a.nchunks == 0)
-        return hipSuccess;
-    return a.bits == 4 ? launch_decode_b<4>(a, st) : launch_decode_b<2>(a, st);
+    DecodeItem chunk[kMaxGroup];
+    int k = 0;
+    int64_t tq = 0;
+    for (int i = 0; i <= count; ++i) {
+        if (i < count && items[i].n > 0) {
+            chunk[k++] = items[i];
+            tq += items[i].n / 4;
+        }
+        if ((k == kMaxGroup || i == count) && k > 0) {
+            hipError_t e = bits == 4 ? decode_b<4>(chunk, k, group, tq, st)
+                                     : decode_b<2>(chunk, k, group, tq, st);
+            if (e != hipSuccess)
+                return e;
+            k = 0;
+            tq = 0;
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, float *base, float *err,

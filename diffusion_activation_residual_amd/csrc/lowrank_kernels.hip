@@ -36,10 +36,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kGramRows = 64;     // rows of M per Gram work-group
-constexpr int kApplyRows = 256;   // rows of M per apply work-group
-constexpr int kAqRows = 64;       // rows of A per A*Q work-group (4 waves x 16)
-constexpr int kAtyCols = 64;      // columns of A per A^T*Y work-group (4 waves x 16)
+constexpr int kGramRows = 256;    // rows of M per Gram work-group (64 per wave)
+constexpr int kApplyRows = 256;   // rows of M per apply work-group (64 per wave)
+constexpr int kCholThreads = 64;  // the r x r factorisation runs on one wavefront
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -73,7 +72,7 @@ Layout make_layout(int64_t m, int64_t n, int r)
 {
     Layout L;
     L.rp = r <= 16 ? 16 : 32;
-    L.mp = round_up(m, 64);
+    L.mp = round_up(m, 128);
     L.np = round_up(n, 64);
     const int64_t lmax = m > n ? m : n;
     L.gram_blocks = (lmax + kGramRows - 1) / kGramRows;
@@ -89,11 +88,36 @@ Layout make_layout(int64_t m, int64_t n, int r)
     return L;
 }
 
+// ------------------------------------------------------------------ buffer loads
+
+// Raw buffer loads: the hardware returns zeros for offsets at or beyond
+// num_records, so masked lanes and tiles past the end need no branch (which
+// keeps the loads of the software pipelines below in flight across steps).
+constexpr uint32_t kBufWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
+constexpr uint32_t kOOB = 0x80000000u;        // any offset >= num_records
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
+}
+
+__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2 /*nt*/));
+}
+
 // ------------------------------------------------------------------ Y = A Q
 
-// One work-group: 64 rows of A (wave w owns rows 16w..16w+15) against all of Q.
-// OUT_OPS: write Y in operand layout (hi/lo planes, rows up to mp, zero beyond m).
-// Otherwise write Y as fp32 [m][r].
+constexpr int kPipe = 4;                        // register stages of the A-streaming pipelines
+constexpr int kAqTiles = 2;                     // 16-row MFMA tiles per wave
+constexpr int kAqRows = 4 * 16 * kAqTiles;      // rows of A per work-group
+
+// One work-group: kAqRows rows of A against all of Q, 64 columns of A per step.
+// Pipeline: A tiles two steps ahead in two statically named register stages
+// (the loop is unrolled by two so no register is copied), Q tiles one step
+// ahead in registers and double-buffered in LDS, one barrier per step.
+// OUT_OPS: write Y in operand layout (hi/lo planes, rows up to mp, zero beyond
+// m); otherwise write Y as fp32 [m][r].
 template <int RP, bool OUT_OPS>
 __global__ void __launch_bounds__(kThreads)
 lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
@@ -101,106 +125,149 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
 {
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
-    const uint16_t *Ab = A + (int64_t)b * m * n;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
     const bf16x8 *qhi = (const bf16x8 *)(wsb + off_qops);
     const bf16x8 *qlo = qhi + (np / 8) * RP;
 
-    __shared__ bf16x8 sq[2][8][RP];
+    __shared__ bf16x8 sq[2][2][8][RP];  // [buffer][hi, lo][k block][column]
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
-    const int64_t row = (int64_t)blk * kAqRows + wave * 16 + li;
-    const bool row_ok = row < m;
-    const uint16_t *arow = Ab + (row_ok ? row : 0) * n;
+    const int64_t row0 = (int64_t)blk * kAqRows;
+    const int64_t rows_here = (m - row0 < kAqRows) ? m - row0 : kAqRows;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (int64_t)b * m * n + row0 * n, (uint32_t)(rows_here * n * 2));
 
     constexpr int QE = 2 * 8 * RP;                 // 16-byte entries of one Q tile
     constexpr int QPT = (QE + kThreads - 1) / kThreads;
+    const int64_t last_tile = np - 64;             // Q loads past the end re-read a valid tile
 
-    auto load_a = [&](int64_t k0, bf16x8 &a0, bf16x8 &a1) {
-        const int64_t c0 = k0 + 8 * g, c1 = k0 + 32 + 8 * g;
-        a0 = (row_ok && c0 < n) ? __builtin_nontemporal_load((const bf16x8 *)(arow + c0)) : bf16x8{};
-        a1 = (row_ok && c1 < n) ? __builtin_nontemporal_load((const bf16x8 *)(arow + c1)) : bf16x8{};
+    auto a_off = [&](int t, int64_t col) -> uint32_t {
+        const int64_t rr = wave * 16 * kAqTiles + t * 16 + li;
+        return (rr < rows_here && col < n) ? (uint32_t)((rr * n + col) * 2) : kOOB;
     };
-    auto load_q = [&](int64_t k0, bf16x8 *qv) {
+    auto load_a = [&](int64_t k0, bf16x8 (&av)[kAqTiles][2]) {
+#pragma unroll
+        for (int t = 0; t < kAqTiles; ++t) {
+            av[t][0] = buf_load16(ra, a_off(t, k0 + 8 * g));
+            av[t][1] = buf_load16(ra, a_off(t, k0 + 32 + 8 * g));
+        }
+    };
+    auto load_q = [&](int64_t k0, bf16x8 (&qv)[QPT]) {
+        const int64_t kt = (k0 < last_tile ? k0 : last_tile) / 8;
 #pragma unroll
         for (int p = 0; p < QPT; ++p) {
             const int e = threadIdx.x + p * kThreads;
-            if (e < QE) {
-                const int hl = e / (8 * RP), rem = e % (8 * RP), kb = rem / RP, c = rem % RP;
-                qv[p] = (hl ? qlo : qhi)[(k0 / 8 + kb) * RP + c];
-            }
+            const int ee = e < QE ? e : 0;
+            const int hl = ee / (8 * RP), rem = ee % (8 * RP), kb = rem / RP, c = rem % RP;
+            qv[p] = (hl ? qlo : qhi)[(kt + kb) * RP + c];
         }
     };
-
-    f32x4 acc[RP / 16];
-#pragma unroll
-    for (int j = 0; j < RP / 16; ++j)
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    bf16x8 a0, a1, qv[QPT];
-    load_a(0, a0, a1);
-    load_q(0, qv);
-    for (int64_t k0 = 0; k0 < n; k0 += 64) {
-        __syncthreads();  // previous tile's readers are done
+    auto store_q = [&](int buf, const bf16x8 (&qv)[QPT]) {
 #pragma unroll
         for (int p = 0; p < QPT; ++p) {
             const int e = threadIdx.x + p * kThreads;
             if (e < QE)
-                (&sq[0][0][0])[e] = qv[p];
+                (&sq[buf][0][0][0])[e] = qv[p];
         }
-        __syncthreads();
-        const bf16x8 c0 = a0, c1 = a1;
-        if (k0 + 64 < n) {  // prefetch the next tile while this one is multiplied
-            load_a(k0 + 64, a0, a1);
-            load_q(k0 + 64, qv);
-        }
+    };
+
+    f32x4 acc[kAqTiles][RP / 16];
 #pragma unroll
-        for (int jt = 0; jt < RP / 16; ++jt) {
-            acc[jt] = mfma(c0, sq[0][g][jt * 16 + li], acc[jt]);
-            acc[jt] = mfma(c0, sq[1][g][jt * 16 + li], acc[jt]);
-            acc[jt] = mfma(c1, sq[0][4 + g][jt * 16 + li], acc[jt]);
-            acc[jt] = mfma(c1, sq[1][4 + g][jt * 16 + li], acc[jt]);
+    for (int t = 0; t < kAqTiles; ++t)
+#pragma unroll
+        for (int j = 0; j < RP / 16; ++j)
+            acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf, const bf16x8 (&av)[kAqTiles][2]) {
+#pragma unroll
+        for (int t = 0; t < kAqTiles; ++t)
+#pragma unroll
+            for (int jt = 0; jt < RP / 16; ++jt) {
+                acc[t][jt] = mfma(av[t][0], sq[buf][0][g][jt * 16 + li], acc[t][jt]);
+                acc[t][jt] = mfma(av[t][0], sq[buf][1][g][jt * 16 + li], acc[t][jt]);
+                acc[t][jt] = mfma(av[t][1], sq[buf][0][4 + g][jt * 16 + li], acc[t][jt]);
+                acc[t][jt] = mfma(av[t][1], sq[buf][1][4 + g][jt * 16 + li], acc[t][jt]);
+            }
+    };
+
+    // Step i multiplies tile i (A stage i % S, LDS buffer i % 2), refills that A
+    // stage with tile i + S, stages Q tile i + 1 into the other LDS buffer and
+    // refills its Q stage with tile i + 1 + S.  What a step waits for was issued
+    // S - 1 steps earlier, so the in-order load counter keeps the loads of the
+    // last S - 1 steps in flight.  The loop is unrolled by S so that every stage
+    // is a fixed set of registers.
+    constexpr int S = kPipe;
+    bf16x8 a[S][kAqTiles][2], q[S][QPT];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        load_q(64 * j, q[j]);
+        load_a(64 * j, a[j]);
+    }
+    store_q(0, q[0]);
+    load_q(64 * S, q[0]);
+    __syncthreads();
+    for (int64_t k0 = 0; k0 < n; k0 += 64 * S) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            compute(j % 2, a[j]);  // zeros past the end of A
+            load_a(k0 + 64 * (j + S), a[j]);
+            store_q((j + 1) % 2, q[(j + 1) % S]);
+            load_q(k0 + 64 * (j + 1 + S), q[(j + 1) % S]);
+            __syncthreads();
         }
     }
 
-    // D layout: lane holds rows 4g..4g+3 of the 16-row tile, column li
-    const int64_t i0 = (int64_t)blk * kAqRows + wave * 16 + 4 * g;
-    if constexpr (OUT_OPS) {
-        bf16x4 *yhi = (bf16x4 *)(wsb + off_out);
-        bf16x4 *ylo = yhi + (mp / 8) * RP * 2;  // bf16x4 units: plane = mp/8 * RP * 8 bf16
-        if (i0 < mp) {
+    // D layout: lane holds rows 4g..4g+3 of each 16-row tile, column li
+#pragma unroll
+    for (int t = 0; t < kAqTiles; ++t) {
+        const int64_t i0 = row0 + wave * 16 * kAqTiles + t * 16 + 4 * g;
+        if constexpr (OUT_OPS) {
+            bf16x4 *yhi = (bf16x4 *)(wsb + off_out);
+            bf16x4 *ylo = yhi + (mp / 8) * RP * 2;  // bf16x4 units: plane = mp/8 * RP * 8 bf16
+            if (i0 < mp) {
+#pragma unroll
+                for (int jt = 0; jt < RP / 16; ++jt) {
+                    bf16x4 h, l;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float y = acc[t][jt][v];
+                        h[v] = (__bf16)y;
+                        l[v] = (__bf16)(y - (float)h[v]);
+                    }
+                    const int64_t idx = ((i0 / 8) * RP + jt * 16 + li) * 2 + ((i0 % 8) / 4);
+                    yhi[idx] = h;
+                    ylo[idx] = l;
+                }
+            }
+        } else {
+            float *out = (float *)(wsb + off_out);
 #pragma unroll
             for (int jt = 0; jt < RP / 16; ++jt) {
-                bf16x4 h, l;
+                const int c = jt * 16 + li;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float y = acc[jt][v];
-                    h[v] = (__bf16)y;
-                    l[v] = (__bf16)(y - (float)h[v]);
-                }
-                const int64_t idx = ((i0 / 8) * RP + jt * 16 + li) * 2 + ((i0 % 8) / 4);
-                yhi[idx] = h;
-                ylo[idx] = l;
+                for (int v = 0; v < 4; ++v)
+                    if (i0 + v < m && c < r)
+                        out[(i0 + v) * r + c] = acc[t][jt][v];
             }
-        }
-    } else {
-        float *out = (float *)(wsb + off_out);
-#pragma unroll
-        for (int jt = 0; jt < RP / 16; ++jt) {
-            const int c = jt * 16 + li;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (i0 + v < m && c < r)
-                    out[(i0 + v) * r + c] = acc[jt][v];
         }
     }
 }
 
 // ------------------------------------------------------------------ Z = A^T Y
 
+constexpr int kAtyCols = 64;  // columns of A per work-group (4 waves x 16)
+
+// LDS row of slab column c.  The 8 loader lanes that hold the same rows of 8
+// different column chunks write columns 8 t + s (t = 0..7); mapping them to rows
+// with distinct low bits puts them in distinct bank groups, and the 8 columns a
+// reader lane group takes (16 consecutive) stay distinct as well.
+__device__ __forceinline__ int slab_col(int c) { return c ^ ((c >> 3) & 7); }
+constexpr int kAtyRows = 64;  // rows of A per pipeline step (two 32-row MFMA k steps)
+
 // One work-group: 64 columns of A (wave w owns columns 16w..16w+15) against all
-// rows.  Each 32-row slab of A is loaded with coalesced 16-byte loads and stored
+// rows.  Each 64-row slab of A is loaded with coalesced 16-byte loads and stored
 // transposed in LDS, so that a lane's MFMA operand (8 consecutive rows of one
-// column) is one 16-byte LDS read.
+// column) is one 16-byte LDS read.  Same pipeline as A Q: slabs two steps ahead
+// in static register stages, Y tiles one step ahead, double-buffered LDS.
 template <int RP>
 __global__ void __launch_bounds__(kThreads)
 lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
@@ -208,60 +275,98 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
 {
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
-    const uint16_t *Ab = A + (int64_t)b * m * n;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
     const bf16x8 *yhi = (const bf16x8 *)(wsb + off_yops);
     const bf16x8 *ylo = yhi + (mp / 8) * RP;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)b * m * n, (uint32_t)(m * n * 2));
 
-    constexpr int SROW = 32 + 8;                  // padded row of the transposed tile (80 B)
-    __shared__ __attribute__((aligned(16))) uint16_t sa[kAtyCols][SROW];
-    __shared__ bf16x8 sy[2][4][RP];
+    constexpr int SROW = kAtyRows + 8;             // padded row of the transposed slab (144 B)
+    __shared__ __attribute__((aligned(16))) uint16_t sa[2][kAtyCols][SROW];
+    __shared__ bf16x8 sy[2][2][kAtyRows / 8][RP];  // [buffer][hi, lo][k block][column]
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
-    // loader role: thread t loads row t/8 of the slab, columns 8*(t%8) .. +7
+    // loader role: thread t loads rows t/8 and t/8 + 32 of the slab, columns 8*(t%8) .. +7
     const int trow = threadIdx.x / 8, tcc = threadIdx.x % 8;
     const int64_t tcol = (int64_t)blk * kAtyCols + 8 * tcc;
-    constexpr int YE = 2 * 4 * RP;
+    constexpr int YE = 2 * (kAtyRows / 8) * RP;
+    constexpr int YPT = (YE + kThreads - 1) / kThreads;
+    const int64_t last_slab = mp - kAtyRows;       // Y loads past the end re-read a valid slab
 
-    auto load_a = [&](int64_t i0) -> u32x4 {
-        const int64_t i = i0 + trow;
-        return (i < m && tcol < n) ? __builtin_nontemporal_load((const u32x4 *)(Ab + i * n + tcol))
-                                   : u32x4{0, 0, 0, 0};
+    auto load_a = [&](int64_t i0, u32x4 (&av)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t i = i0 + trow + 32 * h;
+            const uint32_t off = (i < m && tcol < n) ? (uint32_t)((i * n + tcol) * 2) : kOOB;
+            av[h] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 2 /*nt*/);
+        }
     };
-    auto load_y = [&](int64_t i0) -> bf16x8 {
-        const int e = threadIdx.x;
-        if (e >= YE)
-            return bf16x8{};
-        const int hl = e / (4 * RP), rem = e % (4 * RP), kb = rem / RP, c = rem % RP;
-        return (hl ? ylo : yhi)[(i0 / 8 + kb) * RP + c];
+    auto load_y = [&](int64_t i0, bf16x8 (&yv)[YPT]) {
+        const int64_t kt = (i0 < last_slab ? i0 : last_slab) / 8;
+#pragma unroll
+        for (int p = 0; p < YPT; ++p) {
+            const int e = threadIdx.x + p * kThreads;
+            const int ee = e < YE ? e : 0;
+            const int hl = ee / ((kAtyRows / 8) * RP), rem = ee % ((kAtyRows / 8) * RP);
+            const int kb = rem / RP, c = rem % RP;
+            yv[p] = (hl ? ylo : yhi)[(kt + kb) * RP + c];
+        }
+    };
+    auto store = [&](int buf, const u32x4 (&av)[2], const bf16x8 (&yv)[YPT]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint32_t w = av[h][s >> 1];
+                sa[buf][slab_col(8 * tcc + s)][trow + 32 * h] =
+                    (uint16_t)((s & 1) ? (w >> 16) : (w & 0xffffu));
+            }
+#pragma unroll
+        for (int p = 0; p < YPT; ++p) {
+            const int e = threadIdx.x + p * kThreads;
+            if (e < YE)
+                (&sy[buf][0][0][0])[e] = yv[p];
+        }
     };
 
     f32x4 acc[RP / 16];
 #pragma unroll
     for (int j = 0; j < RP / 16; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int ks = 0; ks < kAtyRows / 32; ++ks) {
+            const bf16x8 aop = *(const bf16x8 *)&sa[buf][slab_col(wave * 16 + li)][32 * ks + 8 * g];
+#pragma unroll
+            for (int jt = 0; jt < RP / 16; ++jt) {
+                acc[jt] = mfma(aop, sy[buf][0][4 * ks + g][jt * 16 + li], acc[jt]);
+                acc[jt] = mfma(aop, sy[buf][1][4 * ks + g][jt * 16 + li], acc[jt]);
+            }
+        }
+    };
 
-    u32x4 av = load_a(0);
-    bf16x8 yv = load_y(0);
-    for (int64_t i0 = 0; i0 < m; i0 += 32) {
-        __syncthreads();
+    // Step i multiplies slab i from LDS buffer i % 2, then stages slab i + 1
+    // (issued S - 1 steps earlier) into the other buffer and refills that
+    // register stage with slab i + 1 + S; unrolled by S as in A Q.
+    constexpr int S = kPipe;
+    u32x4 a[S][2];
+    bf16x8 y[S][YPT];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t w = av[s >> 1];
-            sa[8 * tcc + s][trow] = (uint16_t)((s & 1) ? (w >> 16) : (w & 0xffffu));
-        }
-        if (threadIdx.x < YE)
-            (&sy[0][0][0])[threadIdx.x] = yv;
-        __syncthreads();
-        if (i0 + 32 < m) {
-            av = load_a(i0 + 32);
-            yv = load_y(i0 + 32);
-        }
-        const bf16x8 aop = *(const bf16x8 *)&sa[wave * 16 + li][8 * g];
+    for (int j = 0; j < S; ++j) {
+        load_a(kAtyRows * j, a[j]);
+        load_y(kAtyRows * j, y[j]);
+    }
+    store(0, a[0], y[0]);
+    load_a(kAtyRows * S, a[0]);
+    load_y(kAtyRows * S, y[0]);
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < m; i0 += kAtyRows * S) {
 #pragma unroll
-        for (int jt = 0; jt < RP / 16; ++jt) {
-            acc[jt] = mfma(aop, sy[0][g][jt * 16 + li], acc[jt]);
-            acc[jt] = mfma(aop, sy[1][g][jt * 16 + li], acc[jt]);
+        for (int j = 0; j < S; ++j) {
+            compute(j % 2);
+            store((j + 1) % 2, a[(j + 1) % S], y[(j + 1) % S]);
+            load_a(i0 + kAtyRows * (j + 1 + S), a[(j + 1) % S]);
+            load_y(i0 + kAtyRows * (j + 1 + S), y[(j + 1) % S]);
+            __syncthreads();
         }
     }
 
@@ -277,247 +382,329 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     }
 }
 
+// ------------------------------------------------------------------ fp64 MFMA helpers
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f64_16x16x4_f64: A[i][k] at lane i + 16 k, B[k][j] at lane j + 16 k,
+// D[i][j] at lane j + 16 (i % 4), item i / 4.
+__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c)
+{
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Loads the B operands of M Rinv for every k step and column tile (Rinv upper
+// triangular fp64 [RP][RP]): rb[ks][ct] = Rinv[4 ks + g][16 ct + c].
+template <int RP>
+__device__ __forceinline__ void load_rinv_ops(const double *rinv, int g, int c, double (&rb)[RP / 4][RP / 16])
+{
+#pragma unroll
+    for (int ks = 0; ks < RP / 4; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < RP / 16; ++ct)
+            rb[ks][ct] = rinv[(4 * ks + g) * RP + 16 * ct + c];
+}
+
+// Rows t0..t0+15 of M Rinv (fp64 products of the fp32 rows) in the D layout:
+// item v of lane (c, g) holds row t0 + 4 v + g, column 16 ct + c.
+template <int RP>
+__device__ __forceinline__ void tile_times_rinv(const float *Mb, int64_t L, int r, int64_t t0, int g,
+                                                int c, const double (&rb)[RP / 4][RP / 16],
+                                                f64x4 (&tile)[RP / 16])
+{
+#pragma unroll
+    for (int ct = 0; ct < RP / 16; ++ct)
+        tile[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int64_t row = t0 + c;
+#pragma unroll
+    for (int ks = 0; ks < RP / 4; ++ks) {
+        const int k = 4 * ks + g;
+        const double av = (row < L && k < r) ? (double)Mb[row * r + k] : 0.0;
+#pragma unroll
+        for (int ct = 0; ct < RP / 16; ++ct)
+            if (4 * ks < 16 * ct + 16)  // Rinv is upper triangular: rows past the tile are zero
+                tile[ct] = mfma64(av, rb[ks][ct], tile[ct]);
+    }
+}
+
 // ------------------------------------------------------------------ Gram partials
 
-// Partial G = M'^T M' over kGramRows rows, in fp64, where M' = M (fp32 [L][r]) or,
-// with `rinv` given, M' = M Rinv (Rinv upper triangular fp64 [RP][RP]).
-template <int RP>
+// Partial G = M'^T M' over kGramRows rows in fp64 on MFMA, M' = M (fp32 [L][r])
+// or, with TRANSFORM, M' = M Rinv.  Each wave takes 16-row tiles; tiles in the
+// D layout feed the Gram MFMA directly (A and B hold the same rows per lane
+// group and item, so the k order is consistent).  Only the upper tile pairs are
+// formed; the partial's lower off-diagonal tiles are written as zero.
+template <int RP, bool TRANSFORM>
 __global__ void __launch_bounds__(kThreads)
 lr_gram_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int r,
-               uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, bool transform,
-               size_t off_gram, int blocks_per_mat)
+               uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, size_t off_gram,
+               int blocks_per_mat)
 {
+    constexpr int CT = RP / 16, NP = CT * (CT + 1) / 2;
+    constexpr int WROWS = kGramRows / 4;  // rows per wave
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
     const float *Mb = M + (int64_t)b * m_stride;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, c = lane & 15;
+    __shared__ double sacc[4][RP * RP];
 
-    __shared__ double srow[kGramRows][RP + 1];
-    __shared__ double sR[RP][RP];
-    constexpr int NB = (RP / 4) * (RP / 4);  // 4x4 blocks of G
-    constexpr int RG = kThreads / NB;        // row groups
-    __shared__ double sacc[RG][RP * RP];
+    double rb[RP / 4][RP / 16];
+    if constexpr (TRANSFORM)
+        load_rinv_ops<RP>((const double *)(wsb + off_rinv), g, c, rb);
 
-    // stage the rows as fp64 (zero beyond L and beyond r)
-    for (int e = threadIdx.x; e < kGramRows * RP; e += kThreads) {
-        const int rr = e / RP, c = e % RP;
-        const int64_t row = (int64_t)blk * kGramRows + rr;
-        srow[rr][c] = (row < L && c < r) ? (double)Mb[row * r + c] : 0.0;
-    }
-    if (transform) {
-        const double *rinv = (const double *)(wsb + off_rinv);
-        for (int e = threadIdx.x; e < RP * RP; e += kThreads)
-            (&sR[0][0])[e] = rinv[e];
-        __syncthreads();
-        // TPR threads per row, each producing RP / TPR entries of the transformed row
-        constexpr int TPR = kThreads / kGramRows, PER = RP / TPR;
-        const int rr = threadIdx.x / TPR, part = threadIdx.x % TPR;
-        double outv[PER];
+    f64x4 acc[NP];
 #pragma unroll
-        for (int cc = 0; cc < PER; ++cc) {
-            const int c = part * PER + cc;
-            double s = 0.0;
-            for (int k = 0; k <= c; ++k)
-                s = fma(srow[rr][k], sR[k][c], s);
-            outv[cc] = s;
+    for (int p = 0; p < NP; ++p)
+        acc[p] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int64_t w0 = (int64_t)blk * kGramRows + wave * WROWS;
+    for (int tt = 0; tt < WROWS / 16; ++tt) {
+        const int64_t t0 = w0 + 16 * tt;
+        if (t0 >= L)
+            break;  // per wave; no barrier inside this loop
+        f64x4 tile[CT];
+        if constexpr (TRANSFORM) {
+            tile_times_rinv<RP>(Mb, L, r, t0, g, c, rb, tile);
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t row = t0 + 4 * v + g;
+                    const int col = 16 * ct + c;
+                    tile[ct][v] = (row < L && col < r) ? (double)Mb[row * r + col] : 0.0;
+                }
         }
-        __syncthreads();
+        int p = 0;
 #pragma unroll
-        for (int cc = 0; cc < PER; ++cc)
-            srow[rr][part * PER + cc] = outv[cc];
+        for (int ta = 0; ta < CT; ++ta)
+#pragma unroll
+            for (int tb = ta; tb < CT; ++tb, ++p)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[p] = mfma64(tile[ta][v], tile[tb][v], acc[p]);
     }
-    __syncthreads();
-
-    const int pb = threadIdx.x % NB, rg = threadIdx.x / NB;
-    const int bi = pb / (RP / 4), bj = pb % (RP / 4);
-    double acc[4][4] = {};
-    for (int rr = rg; rr < kGramRows; rr += RG) {
-        double xi[4], xj[4];
+    int p = 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            xi[a] = srow[rr][4 * bi + a];
-            xj[a] = srow[rr][4 * bj + a];
-        }
+    for (int ta = 0; ta < CT; ++ta)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int tb = ta; tb < CT; ++tb, ++p)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                acc[a][c] = fma(xi[a], xj[c], acc[a][c]);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            sacc[rg][(4 * bi + a) * RP + 4 * bj + c] = acc[a][c];
+            for (int v = 0; v < 4; ++v)
+                sacc[wave][(16 * ta + 4 * v + g) * RP + 16 * tb + c] = acc[p][v];
     __syncthreads();
     double *part = (double *)(wsb + off_gram) + (size_t)blk * RP * RP;
     for (int e = threadIdx.x; e < RP * RP; e += kThreads) {
-        double s = 0.0;
-        for (int q = 0; q < RG; ++q)
-            s += sacc[q][e];
-        part[e] = s;
+        const int i = e / RP, j = e % RP;
+        part[e] = (i / 16 <= j / 16) ? (sacc[0][e] + sacc[1][e]) + (sacc[2][e] + sacc[3][e]) : 0.0;
     }
 }
 
 // ------------------------------------------------------------------ Cholesky + inverse
 
-// One work-group per matrix.  Sums the Gram partials in a fixed order, factors
-// G = R^T R (R upper, positive diagonal) in fp64, inverts R.
-// pass 1: store R1 and R1^-1.  pass 2: R = R2 R1, store (R1^-1 R2^-1); write R
-// as fp32 [r][r] into ru_out when it is given.
+// One wavefront per matrix.  Sums the Gram partials in a fixed order, factors
+// G = R^T R (R upper, positive diagonal) in fp64 with lane j holding column j in
+// registers (pivots and multipliers broadcast with readlane), and inverts R by
+// back substitution, again one column per lane.
+// pass 1: store R1 and R1^-1.  pass 2: store (R1^-1 R2^-1) and, when ru_out is
+// given, R = R2 R1 as fp32 [r][r].
 template <int RP>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kCholThreads)
 lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, int gram_blocks,
                int r, int pass, size_t off_r1, size_t off_r1inv, size_t off_rinv,
                float *__restrict__ ru_out)
 {
     const int b = blockIdx.x;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
-    __shared__ double G[RP][RP], R[RP][RP], X[RP][RP], W[RP][RP];
-    __shared__ int dead[RP];
-    __shared__ double tol;
-    const int t = threadIdx.x;
+    __shared__ double G[RP][RP + 1];
+    __shared__ double Rs[RP][RP + 1];
+    __shared__ double S1[RP][RP + 1];  // pass 2: R1^-1
+    __shared__ double rdiag[RP];
+    const int lane = threadIdx.x;
+    constexpr int PER = RP * RP / kCholThreads;
 
+    // 1. sum the partials, entries in flight together, partials in a fixed order
     const double *part = (const double *)(wsb + off_gram);
-    for (int e = t; e < RP * RP; e += kThreads) {
-        double s = 0.0;
-        for (int q = 0; q < gram_blocks; ++q)
-            s += part[(size_t)q * RP * RP + e];
-        (&G[0][0])[e] = s;
-        (&R[0][0])[e] = 0.0;
-        (&X[0][0])[e] = 0.0;
+    double sum[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        sum[e] = 0.0;
+    for (int q = 0; q < gram_blocks; ++q)
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            sum[e] += part[(size_t)q * RP * RP + lane + kCholThreads * e];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = lane + kCholThreads * e;
+        G[idx / RP][idx % RP] = sum[e];
+    }
+    if (pass == 2) {
+        const double *r1inv = (const double *)(wsb + off_r1inv);
+        for (int e = lane; e < RP * RP; e += kCholThreads)
+            S1[e / RP][e % RP] = r1inv[e];
     }
     __syncthreads();
-    if (t == 0) {
-        double tr = 0.0;
-        for (int k = 0; k < r; ++k)
-            tr += G[k][k];
-        tol = 1e-13 * tr / r;
+    double tr = 0.0;
+    for (int k = 0; k < r; ++k)
+        tr += G[k][k];
+    const double tol = 1e-13 * tr / r;
+
+    // 2. factorisation: gc[i] = G[i][lane] for i <= lane, overwritten by R[i][lane].
+    //    Steps k >= r only see zero padding; they run with a zero pivot and change nothing.
+    const bool col = lane < RP;
+    const int lc = col ? lane : 0;
+    uint32_t dead = 0;
+    {
+        double gc[RP];
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            gc[i] = (col && i <= lane) ? G[i][lc] : 0.0;
+#pragma unroll
+        for (int k = 0; k < RP; ++k) {
+            const double dkk = readlane_f64(gc[k], k);
+            const bool bad = k >= r || !(dkk > tol) || !isfinite(dkk);
+            const double rkk = bad ? 0.0 : sqrt(dkk);
+            const double inv = bad ? 0.0 : 1.0 / rkk;
+            dead |= bad ? (1u << k) : 0u;
+            const double rk = (lane == k) ? rkk : (lane > k ? gc[k] * inv : 0.0);
+            gc[k] = rk;
+#pragma unroll
+            for (int i = k + 1; i < RP; ++i) {
+                const double rki = readlane_f64(rk, i);
+                if (lane >= i)
+                    gc[i] = fma(-rki, rk, gc[i]);
+            }
+        }
+        // a dropped column has a zero R column as well; pad columns (>= r) are zero
+        const bool zero_col = !col || ((dead >> lc) & 1u);
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            if (col)
+                Rs[i][lc] = (zero_col || i > lane) ? 0.0 : gc[i];
     }
+    __syncthreads();
+    if (col)
+        rdiag[lc] = ((dead >> lc) & 1u) ? 0.0 : 1.0 / Rs[lc][lc];
     __syncthreads();
 
-    // right-looking Cholesky on the upper triangle
-    for (int k = 0; k < r; ++k) {
-        if (t == 0) {
-            const double d = G[k][k];
-            const bool bad = !(d > tol) || !isfinite(d);
-            dead[k] = bad;
-            R[k][k] = bad ? 0.0 : sqrt(d);
-        }
-        __syncthreads();
-        if (t > k && t < r)
-            R[k][t] = dead[k] ? 0.0 : G[k][t] / R[k][k];
-        __syncthreads();
-        for (int e = t; e < RP * RP; e += kThreads) {
-            const int i = e / RP, j = e % RP;
-            if (i > k && j >= i && j < r)
-                G[i][j] -= R[k][i] * R[k][j];
-        }
-        __syncthreads();
+    // 3. inverse: x[i] = (R^-1)[i][lane]
+    double x[RP];
+#pragma unroll
+    for (int i = RP - 1; i >= 0; --i) {
+        double s = 0.0;
+#pragma unroll
+        for (int k = i + 1; k < RP; ++k)
+            s = fma(Rs[i][k], x[k], s);
+        x[i] = (i == lane) ? rdiag[i] : (i < lane ? -s * rdiag[i] : 0.0);
     }
-    // a dropped column has a zero R column as well
-    for (int e = t; e < RP * RP; e += kThreads) {
-        const int i = e / RP, j = e % RP;
-        if (j < r && dead[j])
-            R[i][j] = 0.0;
-    }
-    __syncthreads();
-    // X = R^-1 by back substitution, one column per thread
-    if (t < r && !dead[t]) {
-        const int c = t;
-        X[c][c] = 1.0 / R[c][c];
-        for (int i = c - 1; i >= 0; --i) {
-            if (dead[i])
-                continue;
-            double s = 0.0;
-            for (int k = i + 1; k <= c; ++k)
-                s += R[i][k] * X[k][c];
-            X[i][c] = -s / R[i][i];
-        }
-    }
-    __syncthreads();
 
     double *r1 = (double *)(wsb + off_r1), *r1inv = (double *)(wsb + off_r1inv);
     double *rinv = (double *)(wsb + off_rinv);
+    if (!col)
+        return;
     if (pass == 1) {
-        for (int e = t; e < RP * RP; e += kThreads) {
-            r1[e] = (&R[0][0])[e];
-            r1inv[e] = (&X[0][0])[e];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            r1[i * RP + lane] = Rs[i][lane];
+            r1inv[i * RP + lane] = x[i];
         }
         return;
     }
-    // pass 2: combined factor R2 R1 and inverse R1^-1 R2^-1 (both upper triangular)
-    for (int e = t; e < RP * RP; e += kThreads) {
-        const int i = e / RP, j = e % RP;
-        double s = 0.0, si = 0.0;
-        for (int k = i; k <= j; ++k) {
-            s += R[i][k] * r1[k * RP + j];
-            si += r1inv[i * RP + k] * X[k][j];
+    // 4. pass 2: column lane of R2 R1 and of R1^-1 R2^-1
+    float *ru = ru_out ? ru_out + (size_t)b * r * r : nullptr;
+    double r1c[RP];
+#pragma unroll
+    for (int k = 0; k < RP; ++k)
+        r1c[k] = r1[k * RP + lane];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        double sw = 0.0, si = 0.0;
+#pragma unroll
+        for (int k = i; k < RP; ++k) {
+            sw = fma(Rs[i][k], r1c[k], sw);
+            si = fma(S1[i][k], x[k], si);
         }
-        W[i][j] = (j >= i) ? s : 0.0;
-        rinv[e] = (j >= i) ? si : 0.0;
-    }
-    __syncthreads();
-    if (ru_out) {
-        float *ru = ru_out + (size_t)b * r * r;
-        for (int e = t; e < r * r; e += kThreads)
-            ru[e] = (float)W[e / r][e % r];
+        rinv[i * RP + lane] = si;
+        if (ru && i < r && lane < r)
+            ru[i * r + lane] = (float)sw;
     }
 }
 
 // ------------------------------------------------------------------ apply M Rinv
 
-// Q = M Rinv row by row (fp64 arithmetic).  Writes Q as fp32 [L][r] into `out`
-// when given, and the operand layout (hi/lo, rows up to Lp, zero beyond L and
-// beyond r) at off_ops when ops is set.
+// Q = M Rinv on fp64 MFMA, 16-row tiles per wave, then through LDS so that the
+// fp32 output is written row by row and every operand slot (8 rows of one
+// column) is one 16-byte store per plane.  Rows L..Lp-1 of the operand layout
+// are written as zeros; columns r..RP-1 are zero.
 template <int RP>
 __global__ void __launch_bounds__(kThreads)
 lr_apply_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_t Lp, int r,
                 uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, bool ops,
                 size_t off_ops, float *__restrict__ out, int64_t out_stride, int blocks_per_mat)
 {
+    constexpr int CT = RP / 16;
+    constexpr int WROWS = kApplyRows / 4;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
     const float *Mb = M + (int64_t)b * m_stride;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
-    __shared__ double sR[RP][RP];
-    const double *rinv = (const double *)(wsb + off_rinv);
-    for (int e = threadIdx.x; e < RP * RP; e += kThreads)
-        (&sR[0][0])[e] = rinv[e];
-    __syncthreads();
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, c = lane & 15;
+    __shared__ float sq[4][16][RP + 1];
 
-    const int64_t row = (int64_t)blk * kApplyRows + threadIdx.x;
-    if (row >= Lp)
-        return;
-    const bool live = row < L;
-    float in[RP];
+    double rb[RP / 4][RP / 16];
+    load_rinv_ops<RP>((const double *)(wsb + off_rinv), g, c, rb);
+    bf16x8 *hi = (bf16x8 *)(wsb + off_ops);
+    bf16x8 *lo = hi + (Lp / 8) * RP;
+    float *ob = out ? out + (int64_t)b * out_stride : nullptr;
+
+    const int64_t w0 = (int64_t)blk * kApplyRows + wave * WROWS;
+    for (int tt = 0; tt < WROWS / 16; ++tt) {
+        const int64_t t0 = w0 + 16 * tt;
+        if (t0 >= Lp)
+            break;  // per wave; only wave-local LDS below
+        f64x4 tile[CT];
+        tile_times_rinv<RP>(Mb, L, r, t0, g, c, rb, tile);
 #pragma unroll
-    for (int k = 0; k < RP; ++k)
-        in[k] = (live && k < r) ? Mb[row * r + k] : 0.0f;
-    float q[RP];
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int c = 0; c < RP; ++c) {
-        double s = 0.0;
+            for (int v = 0; v < 4; ++v)
+                sq[wave][4 * v + g][16 * ct + c] = (float)tile[ct][v];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (ob) {  // 4 lanes per row, RP/4 consecutive columns each
+            const int i = lane >> 2, c0 = (lane & 3) * (RP / 4);
+            const int64_t row = t0 + i;
+            if (row < L)
 #pragma unroll
-        for (int k = 0; k <= c; ++k)
-            s = fma((double)in[k], sR[k][c], s);
-        q[c] = (c < r) ? (float)s : 0.0f;
-    }
-    if (out && live) {
-        float *ob = out + (int64_t)b * out_stride + row * r;
-        for (int c = 0; c < r; ++c)
-            ob[c] = q[c];
-    }
-    if (ops) {
-        __bf16 *hi = (__bf16 *)(wsb + off_ops);
-        __bf16 *lo = hi + Lp * RP;
-        const int64_t base = (row / 8) * RP * 8 + (row % 8);
-#pragma unroll
-        for (int c = 0; c < RP; ++c) {
-            const __bf16 h = (__bf16)q[c];
-            hi[base + c * 8] = h;
-            lo[base + c * 8] = (__bf16)(q[c] - (float)h);
+                for (int cc = 0; cc < RP / 4; ++cc)
+                    if (c0 + cc < r)
+                        ob[row * r + c0 + cc] = sq[wave][i][c0 + cc];
         }
+        if (ops && lane < 2 * RP) {  // one operand slot per lane
+            const int kb = lane / RP, cc = lane % RP;
+            bf16x8 h, l;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float q = sq[wave][8 * kb + i][cc];
+                h[i] = (__bf16)q;
+                l[i] = (__bf16)(q - (float)h[i]);
+            }
+            const int64_t slot = ((t0 >> 3) + kb) * RP + cc;
+            hi[slot] = h;
+            lo[slot] = l;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -529,21 +716,21 @@ hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_s
                     hipStream_t st)
 {
     const int gblocks = (int)((L + kGramRows - 1) / kGramRows);
-    const int Lp_ops = (int)round_up(L, 64);
-    const int ablocks = (Lp_ops + kApplyRows - 1) / kApplyRows;
+    const int64_t Lp_ops = round_up(L, 64);
+    const int ablocks = (int)((Lp_ops + kApplyRows - 1) / kApplyRows);
     const unsigned ggrid = (unsigned)(gblocks * batch), agrid = (unsigned)(ablocks * batch);
-    hipLaunchKernelGGL((lr_gram_kernel<RP>), dim3(ggrid), dim3(kThreads), 0, st, M, m_stride, L,
-                       r, ws, Ly.layer_bytes, Ly.off_r1inv, false, Ly.off_gram, gblocks);
-    hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kThreads), 0, st, ws,
+    hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
+                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks);
+    hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 1, Ly.off_r1, Ly.off_r1inv,
                        Ly.off_rinv, (float *)nullptr);
-    hipLaunchKernelGGL((lr_gram_kernel<RP>), dim3(ggrid), dim3(kThreads), 0, st, M, m_stride, L,
-                       r, ws, Ly.layer_bytes, Ly.off_r1inv, true, Ly.off_gram, gblocks);
-    hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kThreads), 0, st, ws,
+    hipLaunchKernelGGL((lr_gram_kernel<RP, true>), dim3(ggrid), dim3(kThreads), 0, st, M,
+                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks);
+    hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 2, Ly.off_r1, Ly.off_r1inv,
                        Ly.off_rinv, ru);
     hipLaunchKernelGGL((lr_apply_kernel<RP>), dim3(agrid), dim3(kThreads), 0, st, M, m_stride, L,
-                       (int64_t)Lp_ops, r, ws, Ly.layer_bytes, Ly.off_rinv, ops, Ly.off_qops, out,
+                       Lp_ops, r, ws, Ly.layer_bytes, Ly.off_rinv, ops, Ly.off_qops, out,
                        out_stride, ablocks);
     return hipGetLastError();
 }

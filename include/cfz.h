@@ -133,6 +133,25 @@ cfz_status cfz_compress(cfz_state *sender, const uint16_t *x_bf16, uint8_t *code
 cfz_status cfz_decompress(cfz_state *receiver, const uint8_t *codes, const float *scales,
                           uint16_t *xhat_bf16, void *hip_stream);
 
+/* The same steps for `count` separately allocated tensors in as few launches as
+ * possible (up to 16 tensors per launch): e.g. the K and V of one layer, which
+ * the sender has at the same time.  Entry i uses senders[i] / receivers[i] with
+ * x_bf16[i], codes[i], scales[i] (and xhat_bf16[i]; xhat_bf16 itself or any of
+ * its entries may be NULL).  All states must share bits, group, ef_mode and
+ * role, and no state may appear twice; the tensors' buffers must not overlap.
+ * Results are bit-identical to `count` single calls.  All entries are validated
+ * before anything is enqueued; on a validation error nothing is enqueued and
+ * cfz_last_error() names the entry.  count == 0 is a no-op.
+ * Errors: as the single calls, plus CFZ_ERR_SHAPE (count < 0) and CFZ_ERR_MODE
+ * (mixed settings or a repeated state).  CFZ_ERR_HIP may leave the launches
+ * before the failing one enqueued. */
+cfz_status cfz_compress_group(int32_t count, cfz_state *const *senders,
+                              const uint16_t *const *x_bf16, uint8_t *const *codes,
+                              float *const *scales, void *hip_stream);
+cfz_status cfz_decompress_group(int32_t count, cfz_state *const *receivers,
+                                const uint8_t *const *codes, const float *const *scales,
+                                uint16_t *const *xhat_bf16, void *hip_stream);
+
 /* Workspace for cfz_lowrank, in bytes, or 0 if the sizes are invalid. */
 size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r);
 
@@ -146,7 +165,7 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
  * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn).
  * U: [batch][m][r], V: [batch][n][r], RU: [batch][r][r], fp32 outputs.
  * Requires 1 <= r <= 32, r <= m, r <= n, T >= 0, n a multiple of 8 (rows of A
- * are 16-byte aligned), m, n, batch <= 2^20, batch >= 0 (0 is a no-op); a
+ * are 16-byte aligned), m, n, batch <= 2^20, m * n <= 2^30, batch >= 0 (0 is a no-op); a
  * workspace of cfz_lowrank_workspace_bytes(batch, m, n, r) bytes, 256-byte
  * aligned, that the call overwrites.  Products use bf16 MFMA with fp32
  * accumulation; Q and A Q enter them split into two bf16 halves (about 16

@@ -14,7 +14,7 @@ MISALIGNED = 0x10008
 
 def test_library_exports_every_declared_function():
     names = cfz.header_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
     assert cfz.cfz_abi_version() == 1
@@ -144,3 +144,41 @@ def test_stream_copy_validation():
 def test_binding_has_same_names_as_header():
     for name in cfz.header_functions():
         assert hasattr(cfz, name), f"binding lacks {name}"
+
+
+def test_group_validation_without_launching():
+    lib = cfz._lib
+    d = cfz.make_desc(4, 64)
+    a = cfz.cfz_state_resume(d, prev=ALIGNED, err=ALIGNED)
+    b = cfz.cfz_state_resume(d, prev=ALIGNED, err=ALIGNED)
+    lit = cfz.cfz_state_resume(cfz.make_desc(4, 64, ef_mode=cfz.CFZ_EF_LITERAL), base=ALIGNED,
+                               err=ALIGNED)
+    rcv = cfz.cfz_state_resume(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER), base=ALIGNED)
+    P = C.c_void_p
+
+    def arr(*v):
+        return (P * len(v))(*v)
+
+    try:
+        assert lib.cfz_compress_group(0, None, None, None, None, None) == cfz.CFZ_OK
+        assert lib.cfz_compress_group(-1, None, None, None, None, None) == cfz.CFZ_ERR_SHAPE
+        assert lib.cfz_compress_group(2, None, arr(ALIGNED, ALIGNED), arr(ALIGNED, ALIGNED),
+                                      arr(ALIGNED, ALIGNED), None) == cfz.CFZ_ERR_NULL
+        # mixed settings, repeated state, wrong role, misaligned entry
+        assert lib.cfz_compress_group(2, arr(a, lit), arr(ALIGNED, ALIGNED), arr(ALIGNED, ALIGNED),
+                                      arr(ALIGNED, ALIGNED), None) == cfz.CFZ_ERR_MODE
+        assert lib.cfz_compress_group(2, arr(a, a), arr(ALIGNED, ALIGNED), arr(ALIGNED, ALIGNED),
+                                      arr(ALIGNED, ALIGNED), None) == cfz.CFZ_ERR_MODE
+        assert lib.cfz_compress_group(1, arr(rcv), arr(ALIGNED), arr(ALIGNED), arr(ALIGNED),
+                                      None) == cfz.CFZ_ERR_MODE
+        st = lib.cfz_compress_group(2, arr(a, b), arr(ALIGNED, ALIGNED), arr(ALIGNED, MISALIGNED),
+                                    arr(ALIGNED, ALIGNED), None)
+        assert st == cfz.CFZ_ERR_ALIGN and "entry 1" in cfz.cfz_last_error()
+        assert lib.cfz_decompress_group(1, arr(a), arr(ALIGNED), arr(ALIGNED), None,
+                                        None) == cfz.CFZ_ERR_MODE
+        assert lib.cfz_decompress_group(1, arr(rcv), arr(ALIGNED), arr(ALIGNED), arr(MISALIGNED),
+                                        None) == cfz.CFZ_ERR_ALIGN
+        assert cfz.cfz_state_steps(a) == 0 and cfz.cfz_state_steps(b) == 0
+    finally:
+        for h in (a, b, lit, rcv):
+            cfz.cfz_state_destroy(h)

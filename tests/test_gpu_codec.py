@@ -232,7 +232,8 @@ def test_runs_on_a_side_stream():
 
 def test_flux_int4_full_size_sampled_tensors():
     """FLUX.1-dev share, 57 layers x {K, V} of 1024 x 3072, int4 g64, DELTA, 28 steps, in the
-    per-tensor launch configuration of the benchmark; layers 0, 28, 56 compared every step."""
+    launch configuration of the benchmark (one grouped launch per layer for its K and V);
+    layers 0, 28 and 56 are compared every step."""
     sp = SPECS["flux"]
     st = AR1Stream.from_spec(sp, seed=0, device=DEV)
     picks = [0, 1, 56, 57, 112, 113]
@@ -245,14 +246,19 @@ def test_flux_int4_full_size_sampled_tensors():
     or_ = [oracle.Receiver(n, 4, 64, x0=u16(x[i])) for i in picks]
     for t in range(1, sp.steps):
         x = st.next()
+        for j in range(0, len(picks), 2):  # K and V of one layer per grouped call
+            pair = (j, j + 1)
+            cfz.cfz_compress_group([gs[k].handle for k in pair],
+                                   [x[picks[k]].contiguous() for k in pair],
+                                   [gs[k].codes for k in pair], [gs[k].scales for k in pair])
+            cfz.cfz_decompress_group([gr[k].handle for k in pair], [gs[k].codes for k in pair],
+                                     [gs[k].scales for k in pair])
+        torch.cuda.synchronize()
         for j, i in enumerate(picks):
-            codes, scales = gs[j].compress(x[i].contiguous())
-            gr[j].decompress(codes, scales)
             oc, osc = os_[j].compress(u16(x[i]))
             or_[j].decompress(oc, osc)
-            torch.cuda.synchronize()
-            _compare_step(f"flux t{t} tensor {i}", gs[j], gr[j], codes, scales, os_[j], or_[j],
-                          oc, osc)
+            _compare_step(f"flux t{t} tensor {i}", gs[j], gr[j], gs[j].codes, gs[j].scales,
+                          os_[j], or_[j], oc, osc)
 
 
 def _batched_rows_parity(spec_name, bits, group, steps, row_slices, tag):
@@ -331,3 +337,38 @@ def test_graph_replay_matches_oracle_every_replay():
         oc, osc = os_.compress(u16(xs[t]))
         or_.decompress(oc, osc)
         _compare_step(f"graph replay {t}", gs, gr, gs.codes, gs.scales, os_, or_, oc, osc)
+
+
+@pytest.mark.parametrize("bits,group,mode", [(4, 64, 0), (2, 32, 0), (4, 128, 1), (2, 8, 2)])
+def test_grouped_launch_matches_oracle(bits, group, mode):
+    """Separately allocated tensors of different sizes (one empty) in grouped calls: more than
+    16 tensors, so the call spans several launches, and both launch shapes (big and small)."""
+    shapes = [(1024, 1024)] * 17 + [(300, 256), (0, 256), (17, 128), (64, 1024)]
+    say(f"[gpu] grouped b{bits} g{group} m{mode}: {len(shapes)} tensors")
+    seqs = [[x[0] for x in _ar1(r, c, 4, seed=100 + i)] if r else None
+            for i, (r, c) in enumerate(shapes)]
+    snd, rcv, osnd, orcv, xh = [], [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        x0 = seqs[i][0].to(DEV) if r else None
+        snd.append(cfz.Sender(r, c, bits, group, mode, x0=x0))
+        rcv.append(cfz.Receiver(r, c, bits, group, x0=x0))
+        osnd.append(oracle.Sender(r * c, bits, group, MODE_PAIRS[mode],
+                                  x0=u16(seqs[i][0]) if r else None))
+        orcv.append(oracle.Receiver(r * c, bits, group, x0=u16(seqs[i][0]) if r else None))
+        xh.append(torch.empty(r * c, dtype=torch.bfloat16, device=DEV))
+    for t in range(1, 4):
+        xs = [seqs[i][t].to(DEV) if r else torch.empty(0, dtype=torch.bfloat16, device=DEV)
+              for i, (r, c) in enumerate(shapes)]
+        cfz.cfz_compress_group([s.handle for s in snd], xs, [s.codes for s in snd],
+                               [s.scales for s in snd])
+        cfz.cfz_decompress_group([r_.handle for r_ in rcv], [s.codes for s in snd],
+                                 [s.scales for s in snd], xh)
+        torch.cuda.synchronize()
+        for i, (r, c) in enumerate(shapes):
+            if r == 0:
+                continue
+            oc, osc = osnd[i].compress(u16(seqs[i][t]))
+            ox = orcv[i].decompress(oc, osc, want_xhat=True)
+            _compare_step(f"group t{t} entry {i}", snd[i], rcv[i], snd[i].codes, snd[i].scales,
+                          osnd[i], orcv[i], oc, osc, xh[i], ox)
+    assert all(cfz.cfz_state_steps(s.handle) == 3 for s in snd)
