@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--launch", choices=("layer", "tensor", "step"), default="layer",
                     help="tensors per launch: K+V of a layer (default), one, or the whole step")
     ap.add_argument("--no-modes", action="store_true", help="skip the other launch granularities")
+    ap.add_argument("--pool", type=int, default=29,
+                    help="distinct pre-generated steps kept in HBM (inputs cycle through them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} is not "
@@ -191,7 +193,7 @@ def main():
     n = rows * cols
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
-    slots = min(K + W + 1, 29)
+    slots = max(2, min(K + W + 1, args.pool))
     print(f"[bench] generating {slots} steps of {T} x {rows} x {cols} bf16", file=sys.stderr,
           flush=True)
     gen = AR1Stream.from_spec(sp, seed=0, device=dev)

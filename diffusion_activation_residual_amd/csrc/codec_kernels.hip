@@ -18,9 +18,9 @@
 // barrier.  Every kernel is a pure stream: each byte is read or written once.
 //
 // One launch may cover up to kMaxGroup separately allocated tensors of the same
-// bits/group/mode: a small table in the kernel arguments maps work-group ranges
-// to tensors, so the K and V of a layer (or any set of tensors available at
-// once) cost one launch ramp instead of several.
+// bits/group/mode: a table of per-tensor records in the kernel arguments, one
+// grid row per tensor, so the K and V of a layer (or any set of tensors
+// available at once) cost one launch ramp instead of several.
 //
 // Bit-exactness: fp32 IEEE division for the scale and for r/s, rint (ties to
 // even), and explicit fma for the error and base updates; the library is
@@ -78,41 +78,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // ---------------------------------------------------------------- tensor tables
 
+// One 64-byte record per tensor: a work-group reads its tensor's record with a
+// single scalar load (blockIdx.y is the tensor, blockIdx.x the block within it;
+// blocks past a smaller tensor's end exit at once).
+struct CompressRec {
+    const uint16_t *x;
+    uint16_t *prev;
+    float *base;
+    float *err;
+    uint8_t *codes;
+    float *scales;
+    int64_t nquads;
+    int64_t pad;
+};
+
+struct DecodeRec {
+    const uint8_t *codes;
+    const float *scales;
+    float *base;
+    uint16_t *xhat;
+    int64_t nquads;
+    int64_t pad[3];
+};
+
 template <int MAXT>
 struct CompressTable {
-    int32_t count;
-    int32_t begin[MAXT + 1];  // first work-group of each tensor; begin[count] = grid size
-    int64_t nquads[MAXT];
-    const uint16_t *x[MAXT];
-    uint16_t *prev[MAXT];
-    float *base[MAXT];
-    float *err[MAXT];
-    uint8_t *codes[MAXT];
-    float *scales[MAXT];
+    CompressRec t[MAXT];
 };
 
 template <int MAXT>
 struct DecodeTable {
-    int32_t count;
-    int32_t begin[MAXT + 1];
-    int64_t nquads[MAXT];
-    const uint8_t *codes[MAXT];
-    const float *scales[MAXT];
-    float *base[MAXT];
-    uint16_t *xhat[MAXT];
+    DecodeRec t[MAXT];
 };
-
-// the tensor a work-group belongs to (uniform, evaluated in scalar registers)
-template <int MAXT>
-__device__ __forceinline__ int find_tensor(const int32_t *begin, int count)
-{
-    int t = 0;
-#pragma unroll
-    for (int i = 1; i < MAXT; ++i)
-        if (i < count && (int)blockIdx.x >= begin[i])
-            t = i;
-    return t;
-}
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -153,15 +150,17 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
     constexpr bool USE_BASE = (MODE == kLiteral || MODE == kOff);
     constexpr bool USE_ERR = (MODE == kDelta || MODE == kLiteral);
 
-    const int t = find_tensor<MAXT>(tab.begin, tab.count);
-    const int64_t nq = tab.nquads[t];
-    const uint16_t *__restrict__ x = tab.x[t];
-    uint16_t *__restrict__ prev = tab.prev[t];
-    float *__restrict__ base = tab.base[t];
-    float *__restrict__ err = tab.err[t];
-    uint8_t *__restrict__ codes = tab.codes[t];
-    float *__restrict__ scales = tab.scales[t];
-    const int64_t q0 = (int64_t)((int)blockIdx.x - tab.begin[t]) * (kBlock * UNROLL) + threadIdx.x;
+    const CompressRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
+    const int64_t nq = rec.nquads;
+    if ((int64_t)blockIdx.x * (kBlock * UNROLL) >= nq)
+        return;  // this tensor is smaller than the grid's widest one
+    const uint16_t *__restrict__ x = rec.x;
+    uint16_t *__restrict__ prev = rec.prev;
+    float *__restrict__ base = rec.base;
+    float *__restrict__ err = rec.err;
+    uint8_t *__restrict__ codes = rec.codes;
+    float *__restrict__ scales = rec.scales;
+    const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
 
     u32x2 xv[UNROLL], pv[UNROLL];
     f32x4 sv[UNROLL], ev[UNROLL];
@@ -245,13 +244,15 @@ template <int BITS, int G, int UNROLL, int MAXT>
 __global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MAXT> tab)
 {
     constexpr int LANES = G / 4;
-    const int t = find_tensor<MAXT>(tab.begin, tab.count);
-    const int64_t nq = tab.nquads[t];
-    const uint8_t *__restrict__ codes = tab.codes[t];
-    const float *__restrict__ scales = tab.scales[t];
-    float *__restrict__ base = tab.base[t];
-    uint16_t *__restrict__ xhat = tab.xhat[t];
-    const int64_t q0 = (int64_t)((int)blockIdx.x - tab.begin[t]) * (kBlock * UNROLL) + threadIdx.x;
+    const DecodeRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
+    const int64_t nq = rec.nquads;
+    if ((int64_t)blockIdx.x * (kBlock * UNROLL) >= nq)
+        return;
+    const uint8_t *__restrict__ codes = rec.codes;
+    const float *__restrict__ scales = rec.scales;
+    float *__restrict__ base = rec.base;
+    uint16_t *__restrict__ xhat = rec.xhat;
+    const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
 
     uint32_t word[UNROLL];
     float sc[UNROLL];
@@ -347,43 +348,22 @@ static inline unsigned grid_for(int64_t items, int64_t per_block)
 // to keep enough bytes in flight; they take four quads per lane instead.
 constexpr int64_t kBigLaunchQuads = (int64_t)4 << 20;
 
-template <int MAXT, typename Table>
-static bool fill_begin(Table &tab, const int64_t *nq, int count, int64_t per_block)
-{
-    tab.count = count;
-    int64_t acc = 0;
-    for (int i = 0; i < count; ++i) {
-        tab.begin[i] = (int32_t)acc;
-        tab.nquads[i] = nq[i];
-        acc += (nq[i] + per_block - 1) / per_block;
-        if (acc > INT32_MAX)
-            return false;
-    }
-    for (int i = count; i <= MAXT; ++i)
-        tab.begin[i] = (int32_t)acc;
-    for (int i = count; i < MAXT; ++i)
-        tab.nquads[i] = 0;
-    return true;
-}
-
 template <int BITS, int G, int MODE, int UNROLL, int MAXT>
 static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t st)
 {
     CompressTable<MAXT> tab{};
-    int64_t nq[MAXT];
+    int64_t widest = 0;
     for (int i = 0; i < count; ++i) {
-        nq[i] = it[i].n / 4;
-        tab.x[i] = it[i].x;
-        tab.prev[i] = it[i].prev;
-        tab.base[i] = it[i].base;
-        tab.err[i] = it[i].err;
-        tab.codes[i] = it[i].codes;
-        tab.scales[i] = it[i].scales;
+        const int64_t nq = it[i].n / 4;
+        tab.t[i] = CompressRec{it[i].x, it[i].prev, it[i].base, it[i].err, it[i].codes,
+                               it[i].scales, nq, 0};
+        widest = nq > widest ? nq : widest;
     }
-    if (!fill_begin<MAXT>(tab, nq, count, (int64_t)kBlock * UNROLL))
+    const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
+    if (blocks > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, UNROLL, MAXT>), dim3(tab.begin[count]),
-                       dim3(kBlock), 0, st, tab);
+    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, UNROLL, MAXT>),
+                       dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
     return hipGetLastError();
 }
 
@@ -448,18 +428,17 @@ template <int BITS, int G, int UNROLL, int MAXT>
 static hipError_t decode_chunk(const DecodeItem *it, int count, hipStream_t st)
 {
     DecodeTable<MAXT> tab{};
-    int64_t nq[MAXT];
+    int64_t widest = 0;
     for (int i = 0; i < count; ++i) {
-        nq[i] = it[i].n / 4;
-        tab.codes[i] = it[i].codes;
-        tab.scales[i] = it[i].scales;
-        tab.base[i] = it[i].base;
-        tab.xhat[i] = it[i].xhat;
+        const int64_t nq = it[i].n / 4;
+        tab.t[i] = DecodeRec{it[i].codes, it[i].scales, it[i].base, it[i].xhat, nq, {0, 0, 0}};
+        widest = nq > widest ? nq : widest;
     }
-    if (!fill_begin<MAXT>(tab, nq, count, (int64_t)kBlock * UNROLL))
+    const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
+    if (blocks > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, UNROLL, MAXT>), dim3(tab.begin[count]),
-                       dim3(kBlock), 0, st, tab);
+    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, UNROLL, MAXT>),
+                       dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
     return hipGetLastError();
 }
 
