@@ -130,7 +130,8 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
     from synth import gaussian_q0, lowrank_batch
 
     A = lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=7, device=dev)
-    out = {"workload": f"{batch} x {m}x{n} bf16, rank-16 + 0.05 noise, T={T}", "per_rank": {}}
+    out = {"workload": f"{batch} x {m}x{n} bf16, rank-16 + 0.05 noise, T={T}", "per_rank": {},
+           "A_layer0": A[0]}
     for r in (8, 16, 32):
         Q0 = gaussian_q0(batch, n, r, seed=r, device=dev)
         U = torch.empty(batch, m, r, device=dev)
@@ -159,6 +160,28 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
             "mfma_TFLOP/s_executed": round(2 * useful_flop / t / 1e12, 2)}
         del ws
     return out
+
+
+def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
+    """The fp64 CPU oracle on one layer per rank; per-call figures scale that by the batch."""
+    import numpy as np
+
+    import oracle
+    from synth import gaussian_q0
+
+    a = A_layer.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    m, n = a.shape
+    res = {"kind": "oracle", "cores": 1, "unit": "ms per call",
+           "sample": f"one {m}x{n} layer per rank, single-threaded fp64 oracle; per-call time "
+                     f"= per-layer time x {batch} (extrapolated)", "per_rank": {}}
+    for r in ranks:
+        q0 = gaussian_q0(1, n, r, seed=r)[0].numpy()
+        t0 = time.perf_counter()
+        oracle.lowrank(a, q0, T)
+        dt = time.perf_counter() - t0
+        res["per_rank"][str(r)] = {"ms_per_layer": round(dt * 1e3, 1),
+                                   "ms_per_call": round(dt * 1e3 * batch, 1)}
+    return res
 
 
 def main():
@@ -380,7 +403,12 @@ def main():
                                                  steps=min(K, 10))
     if not args.no_lowrank:
         print("[bench] subspace-iteration leg", file=sys.stderr, flush=True)
-        line["lowrank"] = bench_lowrank(cfz, torch, dev)
+        lr = bench_lowrank(cfz, torch, dev)
+        a0 = lr.pop("A_layer0")
+        if not args.no_cpu_baseline:
+            print("[bench] CPU oracle baseline (subspace iteration)", file=sys.stderr, flush=True)
+            lr["cpu_baseline"] = lowrank_cpu_baseline(a0, 57)
+        line["lowrank"] = lr
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         sample_tensors = 114
