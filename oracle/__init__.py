@@ -34,9 +34,9 @@ def _load():
     lib.oracle_pack_codes.argtypes = [i64, i32, p, p]
     lib.oracle_unpack_codes.argtypes = [i64, i32, p, p]
     lib.oracle_quantize.argtypes = [i64, i32, i32, p, p, p]
-    lib.oracle_warmup.argtypes = [i64, i32, i32, p, p, p, p]
-    lib.oracle_compress.argtypes = [i64, i32, i32, i32, p, p, p, p, p, p]
-    lib.oracle_decompress.argtypes = [i64, i32, i32, p, p, p, p]
+    lib.oracle_warmup.argtypes = [i64, i32, i32, i32, p, p, p, p]
+    lib.oracle_compress.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p]
+    lib.oracle_decompress.argtypes = [i64, i32, i32, i32, p, p, p, p]
     lib.oracle_bf16_to_f32.argtypes = [i64, p, p]
     lib.oracle_f32_to_bf16.argtypes = [i64, p, p]
     lib.oracle_qr.argtypes = [i64, i32, p, p, p]
@@ -113,45 +113,51 @@ def f32_to_bf16(f: np.ndarray) -> np.ndarray:
 
 
 class Sender:
-    """Sender-side codec state: P (bf16 previous activation), E (fp32 error), X-hat (fp32 base)."""
+    """Sender-side codec state: P (bf16 previous activation), E (carried error), X-hat (base).
 
-    def __init__(self, n, bits=4, group=64, mode=DELTA, x0=None):
+    E and X-hat are fp32 arrays, or bf16 bit patterns (uint16) with ``state_bf16``."""
+
+    def __init__(self, n, bits=4, group=64, mode=DELTA, x0=None, state_bf16=False):
         _check_codec(n, bits, group)
         self.n, self.bits, self.group, self.mode = n, bits, group, mode
+        self.state_bf16 = bool(state_bf16)
+        sdt = np.uint16 if state_bf16 else np.float32
         self.prev = np.zeros(n, np.uint16) if mode in (DELTA, OPENLOOP) else None
-        self.err = np.zeros(n, np.float32) if mode in (DELTA, LITERAL) else None
-        self.base = np.zeros(n, np.float32) if mode in (LITERAL, OFF) else None
+        self.err = np.zeros(n, sdt) if mode in (DELTA, LITERAL) else None
+        self.base = np.zeros(n, sdt) if mode in (LITERAL, OFF) else None
         x0 = None if x0 is None else np.ascontiguousarray(x0, np.uint16).reshape(-1)
-        _load().oracle_warmup(n, mode, SENDER, _ptr(x0), _ptr(self.prev), _ptr(self.base),
-                              _ptr(self.err))
+        _load().oracle_warmup(n, mode, SENDER, self.state_bf16, _ptr(x0), _ptr(self.prev),
+                              _ptr(self.base), _ptr(self.err))
 
     def compress(self, x: np.ndarray):
         x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
         assert x.size == self.n
         codes = np.zeros(self.n * self.bits // 8, dtype=np.uint8)
         scales = np.zeros(self.n // self.group, dtype=np.float32)
-        _load().oracle_compress(self.n, self.bits, self.group, self.mode, _ptr(x),
-                                _ptr(self.prev), _ptr(self.base), _ptr(self.err),
+        _load().oracle_compress(self.n, self.bits, self.group, self.mode, self.state_bf16,
+                                _ptr(x), _ptr(self.prev), _ptr(self.base), _ptr(self.err),
                                 _ptr(codes), _ptr(scales))
         return codes, scales
 
 
 class Receiver:
-    """Receiver-side codec state: X-hat (fp32 base)."""
+    """Receiver-side codec state: X-hat (fp32 base, or bf16 bit patterns with ``state_bf16``)."""
 
-    def __init__(self, n, bits=4, group=64, x0=None):
+    def __init__(self, n, bits=4, group=64, x0=None, state_bf16=False):
         _check_codec(n, bits, group)
         self.n, self.bits, self.group = n, bits, group
-        self.base = np.zeros(n, np.float32)
+        self.state_bf16 = bool(state_bf16)
+        self.base = np.zeros(n, np.uint16 if state_bf16 else np.float32)
         x0 = None if x0 is None else np.ascontiguousarray(x0, np.uint16).reshape(-1)
-        _load().oracle_warmup(n, DELTA, RECEIVER, _ptr(x0), None, _ptr(self.base), None)
+        _load().oracle_warmup(n, DELTA, RECEIVER, self.state_bf16, _ptr(x0), None,
+                              _ptr(self.base), None)
 
     def decompress(self, codes: np.ndarray, scales: np.ndarray, want_xhat=False):
         codes = np.ascontiguousarray(codes, np.uint8)
         scales = np.ascontiguousarray(scales, np.float32)
         xhat = np.zeros(self.n, np.uint16) if want_xhat else None
-        _load().oracle_decompress(self.n, self.bits, self.group, _ptr(codes), _ptr(scales),
-                                  _ptr(self.base), _ptr(xhat))
+        _load().oracle_decompress(self.n, self.bits, self.group, self.state_bf16, _ptr(codes),
+                                  _ptr(scales), _ptr(self.base), _ptr(xhat))
         return xhat
 
 

@@ -39,7 +39,10 @@
  *     <= 1e-13 * ||M||_F^2 / r (or not finite) is dropped: its Q column and its
  *     R row and column are zero;
  *   - the step-7 triangular factor R_U is returned beside U and V, so that the
- *     reconstruction is U R_U V^T = (A Q) Q^T.
+ *     reconstruction is U R_U V^T = (A Q) Q^T;
+ *   - optional bf16 state: the carried error and the base are stored in bf16;
+ *     each update is the same fp32 fmaf, rounded once to bf16 (nearest even),
+ *     and a zero code still leaves the base untouched.
  *
  * Parity of every function here is pinned by the CPU tests (closed forms,
  * hand-derived fixtures, brute force, invariants, exact-rank recovery and the
@@ -146,30 +149,46 @@ void oracle_quantize(int64_t n, int bits, int group, const float *r,
 }
 
 /* ------------------------------------------------------------------ */
+/* State element access: fp32 arrays, or bf16 bit patterns when state_bf16. */
+
+static float state_get(const void *p, int64_t j, int state_bf16)
+{
+    return state_bf16 ? bf16_to_float(((const uint16_t *)p)[j]) : ((const float *)p)[j];
+}
+
+static void state_set(void *p, int64_t j, float v, int state_bf16)
+{
+    if (state_bf16)
+        ((uint16_t *)p)[j] = float_to_bf16(v);
+    else
+        ((float *)p)[j] = v;
+}
+
+/* ------------------------------------------------------------------ */
 /* Warm-up (step 0): the uncompressed activation initialises the state.
  * x0 may be NULL, meaning an all-zero activation. */
 
-void oracle_warmup(int64_t n, int mode, int role, const uint16_t *x0,
-                   uint16_t *prev, float *base, float *err)
+void oracle_warmup(int64_t n, int mode, int role, int state_bf16, const uint16_t *x0,
+                   uint16_t *prev, void *base, void *err)
 {
     for (int64_t j = 0; j < n; ++j) {
         uint16_t h = x0 ? x0[j] : 0;
         if (role == ROLE_RECEIVER) {
-            base[j] = bf16_to_float(h);
+            state_set(base, j, bf16_to_float(h), state_bf16);
             continue;
         }
         if (mode == MODE_DELTA || mode == MODE_OPENLOOP)
             prev[j] = h;
         if (mode == MODE_LITERAL || mode == MODE_OFF)
-            base[j] = bf16_to_float(h);
+            state_set(base, j, bf16_to_float(h), state_bf16);
         if (mode == MODE_DELTA || mode == MODE_LITERAL)
-            err[j] = 0.0f;
+            state_set(err, j, 0.0f, state_bf16);
     }
 }
 
 /* One compressed step at the sender.  Buffers not used by `mode` may be NULL. */
-void oracle_compress(int64_t n, int bits, int group, int mode,
-                     const uint16_t *x, uint16_t *prev, float *base, float *err,
+void oracle_compress(int64_t n, int bits, int group, int mode, int state_bf16,
+                     const uint16_t *x, uint16_t *prev, void *base, void *err,
                      uint8_t *codes, float *scales)
 {
     int qmax = oracle_qmax(bits);
@@ -181,11 +200,11 @@ void oracle_compress(int64_t n, int bits, int group, int mode,
             int64_t j = j0 + i;
             float xj = bf16_to_float(x[j]);
             if (mode == MODE_DELTA)
-                r[i] = (xj - bf16_to_float(prev[j])) + err[j];
+                r[i] = (xj - bf16_to_float(prev[j])) + state_get(err, j, state_bf16);
             else if (mode == MODE_LITERAL)
-                r[i] = (xj - base[j]) + err[j];
+                r[i] = (xj - state_get(base, j, state_bf16)) + state_get(err, j, state_bf16);
             else if (mode == MODE_OFF)
-                r[i] = xj - base[j];
+                r[i] = xj - state_get(base, j, state_bf16);
             else /* MODE_OPENLOOP */
                 r[i] = xj - bf16_to_float(prev[j]);
         }
@@ -195,11 +214,11 @@ void oracle_compress(int64_t n, int bits, int group, int mode,
             int64_t j = j0 + i;
             float qf = (float)q[j];
             if (mode == MODE_DELTA || mode == MODE_LITERAL)
-                err[j] = fmaf(-qf, s, r[i]);
+                state_set(err, j, fmaf(-qf, s, r[i]), state_bf16);
             if (mode == MODE_DELTA || mode == MODE_OPENLOOP)
                 prev[j] = x[j];
             if ((mode == MODE_LITERAL || mode == MODE_OFF) && q[j] != 0)
-                base[j] = fmaf(qf, s, base[j]);
+                state_set(base, j, fmaf(qf, s, state_get(base, j, state_bf16)), state_bf16);
         }
     }
     oracle_pack_codes(n, bits, q, codes);
@@ -209,16 +228,17 @@ void oracle_compress(int64_t n, int bits, int group, int mode,
 
 /* One step at the receiver: decode the payload and advance the base.
  * xhat (bf16 copy of the new base) may be NULL. */
-void oracle_decompress(int64_t n, int bits, int group, const uint8_t *codes,
-                       const float *scales, float *base, uint16_t *xhat)
+void oracle_decompress(int64_t n, int bits, int group, int state_bf16, const uint8_t *codes,
+                       const float *scales, void *base, uint16_t *xhat)
 {
     int8_t *q = (int8_t *)malloc((size_t)n);
     oracle_unpack_codes(n, bits, codes, q);
     for (int64_t j = 0; j < n; ++j) {
         if (q[j] != 0)
-            base[j] = fmaf((float)q[j], scales[j / group], base[j]);
+            state_set(base, j, fmaf((float)q[j], scales[j / group], state_get(base, j, state_bf16)),
+                      state_bf16);
         if (xhat)
-            xhat[j] = float_to_bf16(base[j]);
+            xhat[j] = float_to_bf16(state_get(base, j, state_bf16));
     }
     free(q);
 }

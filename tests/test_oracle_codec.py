@@ -52,26 +52,36 @@ def test_pack_unpack_roundtrip_every_value(bits):
     assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q, bits), q.size, bits), q)
 
 
+def _state_values(c, key, bf16):
+    v = floats(c[key])
+    return to_bf16_bits(v) if bf16 else v
+
+
+def _state_bits(a, bf16):
+    return a if bf16 else bits32(a)
+
+
 @pytest.mark.parametrize("case", sorted(load_ini("compress_steps.ini")))
 def test_compress_fixture(case):
     c = load_ini("compress_steps.ini")[case]
     bits, group, mode = int(c["bits"]), int(c["group"]), MODES[c["mode"]]
+    sb = c.get("state", "f32") == "bf16"
     x = to_bf16_bits(floats(c["x"]))
     n = x.size
-    s = oracle.Sender(n, bits, group, mode)
+    s = oracle.Sender(n, bits, group, mode, state_bf16=sb)
     if s.prev is not None:
         s.prev[:] = to_bf16_bits(floats(c["prev"]))
     if s.err is not None:
-        s.err[:] = floats(c["err"])
+        s.err[:] = _state_values(c, "err", sb)
     if s.base is not None:
-        s.base[:] = floats(c["base"])
+        s.base[:] = _state_values(c, "base", sb)
     codes, scales = s.compress(x)
     assert np.array_equal(codes, hexbytes(c["codes"]))
     assert np.array_equal(bits32(scales), bits32(floats(c["scales"])))
     if "err_out" in c:
-        assert np.array_equal(bits32(s.err), bits32(floats(c["err_out"])))
+        assert np.array_equal(_state_bits(s.err, sb), _state_bits(_state_values(c, "err_out", sb), sb))
     if "base_out" in c:
-        assert np.array_equal(bits32(s.base), bits32(floats(c["base_out"])))
+        assert np.array_equal(_state_bits(s.base, sb), _state_bits(_state_values(c, "base_out", sb), sb))
     if s.prev is not None:
         assert np.array_equal(s.prev, x)
 
@@ -80,11 +90,12 @@ def test_compress_fixture(case):
 def test_decode_fixture(case):
     c = load_ini("decode_steps.ini")[case]
     bits, group = int(c["bits"]), int(c["group"])
-    base = floats(c["base"])
-    r = oracle.Receiver(base.size, bits, group)
+    sb = c.get("state", "f32") == "bf16"
+    base = _state_values(c, "base", sb)
+    r = oracle.Receiver(base.size, bits, group, state_bf16=sb)
     r.base[:] = base
     xhat = r.decompress(hexbytes(c["codes"]), floats(c["scales"]), want_xhat=True)
-    assert np.array_equal(bits32(r.base), bits32(floats(c["base_out"])))
+    assert np.array_equal(_state_bits(r.base, sb), _state_bits(_state_values(c, "base_out", sb), sb))
     assert np.array_equal(xhat, to_bf16_bits(floats(c["xhat"])))
 
 
@@ -355,3 +366,74 @@ def test_checkpoint_resume_and_determinism():
         rcv3.decompress(c, s)
     assert np.array_equal(rcv3.base.view(np.uint32), rcv.base.view(np.uint32))
     assert np.array_equal(snd3.err.view(np.uint32), snd.err.view(np.uint32))
+
+
+# ---------------------------------------------------------------- bf16 state
+
+def _bf16_ulp_half(v):
+    """Half a bf16 ulp at |v| (for normal numbers; at least the smallest subnormal step)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.maximum(2.0 ** (e - 8), 2.0 ** -134)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (2, 32)])
+def test_bf16_state_closed_loop_sync_and_bound(bits, group):
+    """OFF mode with bf16 bases: sender and receiver stay bit-identical, and the receiver is
+    within half a quantization step plus half a bf16 ulp of every activation."""
+    steps = 12
+    sp = SPECS["tiny"]
+    stream = AR1Stream(1, 256, 512, sp.alpha, sp.noise, 0.0, seed=3, key="tiny")
+    xs = [bf16_np(stream.next()) for _ in range(steps)]
+    n = xs[0].size
+    snd = oracle.Sender(n, bits, group, oracle.OFF, x0=xs[0], state_bf16=True)
+    rcv = oracle.Receiver(n, bits, group, x0=xs[0], state_bf16=True)
+    for t in range(1, steps):
+        codes, scales = snd.compress(xs[t])
+        rcv.decompress(codes, scales)
+        assert np.array_equal(snd.base, rcv.base)
+        b = bf16_bits_to_f64(rcv.base)
+        s = np.repeat(scales.astype(np.float64), group)
+        err = np.abs(bf16_bits_to_f64(xs[t]) - b)
+        assert np.all(err <= s / 2 * (1 + 2.0 ** -20) + _bf16_ulp_half(b) * 1.0001)
+
+
+def test_bf16_state_zero_residual_and_error_bound():
+    rng = np.random.default_rng(4)
+    n = 4096
+    x0 = oracle.f32_to_bf16(rng.standard_normal(n).astype(np.float32))
+    for mode in (oracle.DELTA, oracle.LITERAL, oracle.OFF):
+        s = oracle.Sender(n, 4, 64, mode, x0=x0, state_bf16=True)
+        before = [None if b is None else b.copy() for b in (s.prev, s.err, s.base)]
+        codes, scales = s.compress(x0)
+        assert not codes.any() and not scales.any()
+        for b, a in zip(before, (s.prev, s.err, s.base)):
+            if b is not None:
+                assert np.array_equal(b, a)
+    # DELTA with a bf16 error buffer: |E| <= s/2 up to its bf16 rounding
+    sp = SPECS["flux"]
+    stream = AR1Stream(1, 256, 512, sp.alpha, sp.noise, 0.01, seed=0, key="flux")
+    xs = [bf16_np(stream.next()) for _ in range(6)]
+    snd = oracle.Sender(xs[0].size, 4, 64, oracle.DELTA, x0=xs[0], state_bf16=True)
+    for t in range(1, 6):
+        codes, scales = snd.compress(xs[t])
+        e = np.abs(bf16_bits_to_f64(snd.err))
+        s = np.repeat(scales.astype(np.float64), 64)
+        assert np.all(e <= s / 2 * (1 + 2.0 ** -8) + 2.0 ** -133)
+
+
+@pytest.mark.parametrize("mode", [oracle.DELTA, oracle.OFF])
+def test_bf16_state_accuracy_matches_fp32_state(mode):
+    """Keeping the state in bf16 changes the reconstruction error by well under 5% here."""
+    def final_err(sb):
+        sp = SPECS["flux"]
+        stream = AR1Stream(1, 256, 512, sp.alpha, sp.noise, 0.01, seed=0, key="flux")
+        xs = [bf16_np(stream.next()) for _ in range(28)]
+        snd = oracle.Sender(xs[0].size, 4, 64, mode, x0=xs[0], state_bf16=sb)
+        rcv = oracle.Receiver(xs[0].size, 4, 64, x0=xs[0], state_bf16=sb)
+        for t in range(1, 28):
+            rcv.decompress(*snd.compress(xs[t]))
+        b = bf16_bits_to_f64(rcv.base) if sb else rcv.base.astype(np.float64)
+        xt = bf16_bits_to_f64(xs[-1])
+        return np.linalg.norm(xt - b) / np.linalg.norm(xt)
+    e32, e16 = final_err(False), final_err(True)
+    assert abs(e16 - e32) <= 0.05 * e32
