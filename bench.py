@@ -30,12 +30,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def algorithmic_bytes(bits, group, mode="delta"):
-    """Bytes per element each kernel must move with the state layout of the library."""
+def algorithmic_bytes(bits, group, mode="delta", state_bf16=False):
+    """Bytes per element each kernel must move with the state layout of the library
+    (carried error and base 4 bytes each in fp32 state, 2 in bf16 state)."""
     payload = bits / 8 + 4 / group
-    state = {"delta": 2 + 2 + 4 + 4, "literal": 4 + 4 + 4 + 4, "off": 4 + 4}[mode]
+    w = 2 if state_bf16 else 4
+    state = {"delta": 2 + 2 + w + w, "literal": 4 * w, "off": 2 * w}[mode]
     compress = 2 + state + payload           # read x, read+write state, write payload
-    decode = payload + 4 + 4                 # read payload, read+write fp32 base
+    decode = payload + 2 * w                 # read payload, read+write base
     return compress, decode
 
 
@@ -196,6 +198,8 @@ def main():
     ap.add_argument("--launch", choices=("layer", "tensor", "step"), default="layer",
                     help="tensors per launch: K+V of a layer (default), one, or the whole step")
     ap.add_argument("--no-modes", action="store_true", help="skip the other launch granularities")
+    ap.add_argument("--no-bf16-state", action="store_true",
+                    help="skip the leg with the carried error and base held in bf16")
     ap.add_argument("--pool", type=int, default=29,
                     help="distinct pre-generated steps kept in HBM (inputs cycle through them)")
     args = ap.parse_args()
@@ -231,12 +235,18 @@ def main():
     base = torch.empty((T, n), dtype=torch.float32, device=dev)
     codes = torch.empty((T, n * bits // 8), dtype=torch.uint8, device=dev)
     scales = torch.empty((T, n // group), dtype=torch.float32, device=dev)
-    sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER)
-    rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
+    half = {}  # bf16 carried error and base, allocated on first use
 
-    def fresh_states():
-        s_ = [cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)]
-        r_ = [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)]
+    def fresh_states(sb=False):
+        sdt = cfz.CFZ_STATE_BF16 if sb else cfz.CFZ_STATE_F32
+        if sb and not half:
+            half["err"] = torch.empty((T, n), dtype=torch.bfloat16, device=dev)
+            half["base"] = torch.empty((T, n), dtype=torch.bfloat16, device=dev)
+        e_, b_ = (half["err"], half["base"]) if sb else (err, base)
+        sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER, sdt)
+        rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER, sdt)
+        s_ = [cfz.cfz_state_create(sd, prev=prev[i], err=e_[i], x0=X[0, i]) for i in range(T)]
+        r_ = [cfz.cfz_state_create(rd, base=b_[i], x0=X[0, i]) for i in range(T)]
         return s_, r_
 
     def slot_of(step):  # step >= 1; wraps around the pre-generated pool
@@ -245,11 +255,11 @@ def main():
     # tensors per call: 2 = the K and V of one layer, 1 = each tensor alone, T = the whole step
     per_call = {"layer": 2, "tensor": 1, "step": T}
 
-    def run_mode(mode, K, W, use_graph):
+    def run_mode(mode, K, W, use_graph, sb=False):
         g = per_call[mode]
         calls = [list(range(i, min(i + g, T))) for i in range(0, T, g)]
         launches = sum((len(c) + 15) // 16 for c in calls)
-        snd, rcv = fresh_states()
+        snd, rcv = fresh_states(sb)
 
         def compress_phase(slot):
             for c in calls:
@@ -286,7 +296,7 @@ def main():
             torch.cuda.synchronize()
             for h in snd + rcv:
                 cfz.cfz_state_destroy(h)
-            snd[:], rcv[:] = fresh_states()
+            snd[:], rcv[:] = fresh_states(sb)
             torch.cuda.synchronize()
 
         def run_step(step, ev=None):
@@ -344,6 +354,29 @@ def main():
             "compress_GB/s": round(bc * pe / (r_["t_comp"] / nl) / 1e9, 1),
             "decode_GB/s": round(bd * pe / (r_["t_dec"] / nl) / 1e9, 1)}
 
+    # the same per-layer launches with the carried error and the base held in bf16
+    bf16_state = None
+    if not args.no_bf16_state:
+        print("[bench] bf16-state leg", file=sys.stderr, flush=True)
+        kb = min(K, 10)
+        r_ = run_mode(args.launch, kb, 1, not args.no_graph, sb=True)
+        bc16, bd16 = algorithmic_bytes(bits, group, state_bf16=True)
+        nl = kb * r_["launches"]
+        pe = n * T / r_["launches"]
+        c16 = bc16 * pe / (r_["t_comp"] / nl) / 1e9
+        d16 = bd16 * pe / (r_["t_dec"] / nl) / 1e9
+        bf16_state = {
+            "workload": f"{T} tensors of {rows}x{cols}, int{bits} g{group}, delta, carried "
+                        "error and base in bf16", "steps": kb,
+            "activation_GB/s": round(2 * n * T * kb / r_["elapsed"] / 1e9, 2),
+            "compress": {"avg_launch_us": round(r_["t_comp"] / nl * 1e6, 3),
+                         "GB/s": round(c16, 1), "frac_hbm_peak": round(c16 / HBM_PEAK_GBS, 4),
+                         "bytes_per_elem": bc16},
+            "decode": {"avg_launch_us": round(r_["t_dec"] / nl * 1e6, 3),
+                       "GB/s": round(d16, 1), "frac_hbm_peak": round(d16 / HBM_PEAK_GBS, 4),
+                       "bytes_per_elem": bd16}}
+        half.clear()
+
     # achievable copy ceiling on a buffer as large as two steps of activations
     src = X[1:3].reshape(-1)
     dst = torch.empty_like(src)
@@ -395,6 +428,7 @@ def main():
             "stream_copy_ceiling_GB/s": round(copy_gbs, 1),
         },
         "other_launch_granularities": other_modes,
+        "bf16_state": bf16_state,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
     }
     if not args.no_batched:

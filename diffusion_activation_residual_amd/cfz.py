@@ -23,16 +23,18 @@ CFZ_OK, CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_UNSUPPORTED = 0, 1, 2, 3
 CFZ_ERR_ALIGN, CFZ_ERR_MODE, CFZ_ERR_WORKSPACE, CFZ_ERR_HIP = 4, 5, 6, 7
 CFZ_EF_DELTA, CFZ_EF_LITERAL, CFZ_EF_OFF = 0, 1, 2
 CFZ_SENDER, CFZ_RECEIVER = 0, 1
+CFZ_STATE_F32, CFZ_STATE_BF16 = 0, 1
 MODES = {"delta": CFZ_EF_DELTA, "literal": CFZ_EF_LITERAL, "off": CFZ_EF_OFF}
 
 
 class cfz_desc(C.Structure):
     _fields_ = [("rows", C.c_int64), ("cols", C.c_int64), ("bits", C.c_int32),
-                ("group", C.c_int32), ("ef_mode", C.c_int32), ("role", C.c_int32)]
+                ("group", C.c_int32), ("ef_mode", C.c_int32), ("role", C.c_int32),
+                ("state_dtype", C.c_int32), ("reserved", C.c_int32)]
 
 
 class cfz_buffers(C.Structure):
-    _fields_ = [("prev_bf16", C.c_void_p), ("base_f32", C.c_void_p), ("err_f32", C.c_void_p)]
+    _fields_ = [("prev_bf16", C.c_void_p), ("base", C.c_void_p), ("err", C.c_void_p)]
 
 
 class CfzError(RuntimeError):
@@ -132,8 +134,9 @@ def cfz_last_error() -> str:
     return _lib.cfz_last_error().decode(errors="replace")
 
 
-def make_desc(rows, cols, bits=4, group=64, ef_mode=CFZ_EF_DELTA, role=CFZ_SENDER) -> cfz_desc:
-    return cfz_desc(rows, cols, bits, group, ef_mode, role)
+def make_desc(rows, cols, bits=4, group=64, ef_mode=CFZ_EF_DELTA, role=CFZ_SENDER,
+              state_dtype=CFZ_STATE_F32) -> cfz_desc:
+    return cfz_desc(rows, cols, bits, group, ef_mode, role, state_dtype, 0)
 
 
 def cfz_codes_bytes(desc: cfz_desc) -> int:
@@ -224,16 +227,24 @@ def cfz_stream_copy(src, dst, nbytes=None, stream=None) -> None:
 
 # ------------------------------------------------------------------ torch-owned state helpers
 
+def _state_torch_dtype(state_bf16):
+    return torch.bfloat16 if state_bf16 else torch.float32
+
+
 class Sender:
-    """A sender's codec state with its buffers held in torch device tensors."""
+    """A sender's codec state with its buffers held in torch device tensors.
+
+    ``state_bf16`` keeps the carried error and the base in bf16 instead of fp32."""
 
     def __init__(self, rows, cols, bits=4, group=64, mode=CFZ_EF_DELTA, x0=None,
-                 device="cuda", stream=None):
-        self.desc = make_desc(rows, cols, bits, group, mode, CFZ_SENDER)
+                 device="cuda", stream=None, state_bf16=False):
+        self.desc = make_desc(rows, cols, bits, group, mode, CFZ_SENDER,
+                              CFZ_STATE_BF16 if state_bf16 else CFZ_STATE_F32)
         n = rows * cols
+        sdt = _state_torch_dtype(state_bf16)
         self.prev = torch.empty(n, dtype=torch.bfloat16, device=device) if mode == CFZ_EF_DELTA else None
-        self.base = torch.empty(n, dtype=torch.float32, device=device) if mode != CFZ_EF_DELTA else None
-        self.err = torch.empty(n, dtype=torch.float32, device=device) if mode != CFZ_EF_OFF else None
+        self.base = torch.empty(n, dtype=sdt, device=device) if mode != CFZ_EF_DELTA else None
+        self.err = torch.empty(n, dtype=sdt, device=device) if mode != CFZ_EF_OFF else None
         self.codes = torch.empty(cfz_codes_bytes(self.desc), dtype=torch.uint8, device=device)
         self.scales = torch.empty(n // group, dtype=torch.float32, device=device)
         self.handle = cfz_state_create(self.desc, self.prev, self.base, self.err, x0, stream)
@@ -259,9 +270,11 @@ class Sender:
 class Receiver:
     """A receiver's codec state (the running base) held in a torch device tensor."""
 
-    def __init__(self, rows, cols, bits=4, group=64, x0=None, device="cuda", stream=None):
-        self.desc = make_desc(rows, cols, bits, group, CFZ_EF_DELTA, CFZ_RECEIVER)
-        self.base = torch.empty(rows * cols, dtype=torch.float32, device=device)
+    def __init__(self, rows, cols, bits=4, group=64, x0=None, device="cuda", stream=None,
+                 state_bf16=False):
+        self.desc = make_desc(rows, cols, bits, group, CFZ_EF_DELTA, CFZ_RECEIVER,
+                              CFZ_STATE_BF16 if state_bf16 else CFZ_STATE_F32)
+        self.base = torch.empty(rows * cols, dtype=_state_torch_dtype(state_bf16), device=device)
         self.handle = cfz_state_create(self.desc, None, self.base, None, x0, stream)
 
     def decompress(self, codes, scales, xhat=None, stream=None):

@@ -64,6 +64,10 @@ cfz_status check_desc(const cfz_desc *d)
         return fail(CFZ_ERR_MODE, "ef_mode = %d", d->ef_mode);
     if (d->role != CFZ_SENDER && d->role != CFZ_RECEIVER)
         return fail(CFZ_ERR_MODE, "role = %d", d->role);
+    if (d->state_dtype != CFZ_STATE_F32 && d->state_dtype != CFZ_STATE_BF16)
+        return fail(CFZ_ERR_UNSUPPORTED, "state_dtype = %d", d->state_dtype);
+    if (d->reserved != 0)
+        return fail(CFZ_ERR_SHAPE, "reserved field must be 0");
     return CFZ_OK;
 }
 
@@ -82,15 +86,15 @@ cfz_status check_buffers(const cfz_desc &d, const cfz_buffers *b, cfz_buffers *u
     if (!b)
         return fail(CFZ_ERR_NULL, "buffers is NULL");
     const bool empty = d.rows * d.cols == 0;
-    *used = cfz_buffers{needs_prev(d) ? b->prev_bf16 : nullptr, needs_base(d) ? b->base_f32 : nullptr,
-                        needs_err(d) ? b->err_f32 : nullptr};
+    *used = cfz_buffers{needs_prev(d) ? b->prev_bf16 : nullptr, needs_base(d) ? b->base : nullptr,
+                        needs_err(d) ? b->err : nullptr};
     if (needs_prev(d) && !b->prev_bf16 && !empty)
         return fail(CFZ_ERR_NULL, "prev_bf16 is required by a DELTA sender");
-    if (needs_base(d) && !b->base_f32 && !empty)
-        return fail(CFZ_ERR_NULL, "base_f32 is required by this role/mode");
-    if (needs_err(d) && !b->err_f32 && !empty)
-        return fail(CFZ_ERR_NULL, "err_f32 is required by this mode");
-    if (!aligned16(used->prev_bf16) || !aligned16(used->base_f32) || !aligned16(used->err_f32))
+    if (needs_base(d) && !b->base && !empty)
+        return fail(CFZ_ERR_NULL, "base is required by this role/mode");
+    if (needs_err(d) && !b->err && !empty)
+        return fail(CFZ_ERR_NULL, "err is required by this mode");
+    if (!aligned16(used->prev_bf16) || !aligned16(used->base) || !aligned16(used->err))
         return fail(CFZ_ERR_ALIGN, "state buffers must be 16-byte aligned");
     return CFZ_OK;
 }
@@ -185,7 +189,8 @@ cfz_status cfz_state_create(const cfz_desc *desc, const cfz_buffers *bufs, const
     if (!s)
         return fail(CFZ_ERR_NULL, "out of host memory");
     const int64_t nchunks = desc->rows * desc->cols / 8;
-    hipError_t e = cfz::launch_warmup(x0, used.prev_bf16, used.base_f32, used.err_f32, nchunks,
+    hipError_t e = cfz::launch_warmup(x0, used.prev_bf16, used.base, used.err,
+                                      desc->state_dtype == CFZ_STATE_BF16, nchunks,
                                       (hipStream_t)stream);
     if (e != hipSuccess) {
         s->magic = 0;
@@ -230,8 +235,7 @@ static cfz_status check_compress_one(cfz_state *s, const uint16_t *x, uint8_t *c
         return fail(CFZ_ERR_NULL, "x, codes and scales are required");
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
         return fail(CFZ_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
-    *item = cfz::CompressItem{x, s->bufs.prev_bf16, s->bufs.base_f32, s->bufs.err_f32, codes,
-                              scales, n};
+    *item = cfz::CompressItem{x, s->bufs.prev_bf16, s->bufs.base, s->bufs.err, codes, scales, n};
     return CFZ_OK;
 }
 
@@ -249,13 +253,14 @@ static cfz_status check_decode_one(cfz_state *s, const uint8_t *codes, const flo
         return fail(CFZ_ERR_NULL, "codes and scales are required");
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(xhat))
         return fail(CFZ_ERR_ALIGN, "codes, scales and xhat must be 16-byte aligned");
-    *item = cfz::DecodeItem{codes, scales, s->bufs.base_f32, xhat, n};
+    *item = cfz::DecodeItem{codes, scales, s->bufs.base, xhat, n};
     return CFZ_OK;
 }
 
 static bool same_codec(const cfz_desc &a, const cfz_desc &b)
 {
-    return a.bits == b.bits && a.group == b.group && a.ef_mode == b.ef_mode && a.role == b.role;
+    return a.bits == b.bits && a.group == b.group && a.ef_mode == b.ef_mode && a.role == b.role &&
+           a.state_dtype == b.state_dtype;
 }
 
 cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *scales,
@@ -266,7 +271,8 @@ cfz_status cfz_compress(cfz_state *s, const uint16_t *x, uint8_t *codes, float *
     if (st != CFZ_OK)
         return st;
     const cfz_desc &d = s->desc;
-    hipError_t e = cfz::launch_compress(&item, 1, d.bits, d.group, d.ef_mode, (hipStream_t)stream);
+    hipError_t e = cfz::launch_compress(&item, 1, d.bits, d.group, d.ef_mode,
+                                        d.state_dtype == CFZ_STATE_BF16, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "compress launch");
     ++s->steps;
@@ -281,7 +287,8 @@ cfz_status cfz_decompress(cfz_state *s, const uint8_t *codes, const float *scale
     if (st != CFZ_OK)
         return st;
     const cfz_desc &d = s->desc;
-    hipError_t e = cfz::launch_decode(&item, 1, d.bits, d.group, (hipStream_t)stream);
+    hipError_t e = cfz::launch_decode(&item, 1, d.bits, d.group, d.state_dtype == CFZ_STATE_BF16,
+                                      (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");
     ++s->steps;
@@ -303,7 +310,8 @@ static cfz_status check_group(int32_t count, cfz_state *const *states, const voi
         if (st != CFZ_OK)
             return fail_entry(st, i);
         if (!same_codec(states[i]->desc, states[0]->desc))
-            return fail(CFZ_ERR_MODE, "entry %d: bits, group, mode and role must match entry 0", i);
+            return fail(CFZ_ERR_MODE, "entry %d: bits, group, mode, role and state must match entry 0",
+                        i);
         for (int32_t j = 0; j < i; ++j)
             if (states[j] == states[i])
                 return fail(CFZ_ERR_MODE, "entries %d and %d are the same state", j, i);
@@ -326,7 +334,7 @@ cfz_status cfz_compress_group(int32_t count, cfz_state *const *senders, const ui
     if (st == CFZ_OK) {
         const cfz_desc &d = senders[0]->desc;
         hipError_t e = cfz::launch_compress(items, count, d.bits, d.group, d.ef_mode,
-                                            (hipStream_t)stream);
+                                            d.state_dtype == CFZ_STATE_BF16, (hipStream_t)stream);
         if (e != hipSuccess)
             st = hip_fail(e, "grouped compress launch");
         else
@@ -353,7 +361,8 @@ cfz_status cfz_decompress_group(int32_t count, cfz_state *const *receivers,
             st = fail_entry(st, i);
     if (st == CFZ_OK) {
         const cfz_desc &d = receivers[0]->desc;
-        hipError_t e = cfz::launch_decode(items, count, d.bits, d.group, (hipStream_t)stream);
+        hipError_t e = cfz::launch_decode(items, count, d.bits, d.group,
+                                          d.state_dtype == CFZ_STATE_BF16, (hipStream_t)stream);
         if (e != hipSuccess)
             st = hip_fail(e, "grouped decode launch");
         else

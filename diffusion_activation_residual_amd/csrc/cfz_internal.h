@@ -14,8 +14,8 @@ constexpr int kMaxGroup = 16;  // tensors per codec launch
 struct CompressItem {
     const uint16_t *x;
     uint16_t *prev;
-    float *base;
-    float *err;
+    void *base;  // fp32 or bf16 per the state precision
+    void *err;
     uint8_t *codes;
     float *scales;
     int64_t n;  // elements, a multiple of the group size
@@ -24,17 +24,18 @@ struct CompressItem {
 struct DecodeItem {
     const uint8_t *codes;
     const float *scales;
-    float *base;
+    void *base;
     uint16_t *xhat;  // may be null
     int64_t n;
 };
 
 // Any count: tensors are launched kMaxGroup at a time; empty tensors are skipped.
 hipError_t launch_compress(const CompressItem *items, int count, int bits, int group, int mode,
-                           hipStream_t st);
-hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, hipStream_t st);
-hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, float *base, float *err,
-                         int64_t nchunks, hipStream_t st);
+                           bool state_bf16, hipStream_t st);
+hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, bool state_bf16,
+                         hipStream_t st);
+hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, void *base, void *err,
+                         bool state_bf16, int64_t nchunks, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t nvec, hipStream_t st);
 
 struct LowrankArgs {

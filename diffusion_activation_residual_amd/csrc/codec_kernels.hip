@@ -84,8 +84,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 struct CompressRec {
     const uint16_t *x;
     uint16_t *prev;
-    float *base;
-    float *err;
+    void *base;  // fp32 or bf16 state
+    void *err;
     uint8_t *codes;
     float *scales;
     int64_t nquads;
@@ -95,7 +95,7 @@ struct CompressRec {
 struct DecodeRec {
     const uint8_t *codes;
     const float *scales;
-    float *base;
+    void *base;
     uint16_t *xhat;
     int64_t nquads;
     int64_t pad[3];
@@ -123,6 +123,53 @@ __device__ __forceinline__ float bf16_at(const u32x2 &v, int k)
     return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// Four consecutive state values (E or X-hat) of one quad, fp32 (16 bytes) or
+// bf16 (8 bytes).  `raw` keeps the loaded bf16 bits so that a base element with
+// a zero code is stored back bit for bit.
+template <bool SB>
+struct Quad;
+
+template <>
+struct Quad<false> {
+    f32x4 v;
+    __device__ __forceinline__ void load(const void *p, int64_t q, bool live)
+    {
+        v = live ? __builtin_nontemporal_load((const f32x4 *)p + q) : f32x4{0, 0, 0, 0};
+    }
+    __device__ __forceinline__ float get(int k) const { return v[k]; }
+    // stores new[k] where keep[k] is false, the loaded value where it is true
+    __device__ __forceinline__ void store(void *p, int64_t q, const float (&nv)[4],
+                                          const bool (&keep)[4]) const
+    {
+        f32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            o[k] = keep[k] ? v[k] : nv[k];
+        __builtin_nontemporal_store(o, (f32x4 *)p + q);
+    }
+};
+
+template <>
+struct Quad<true> {
+    u32x2 raw;
+    __device__ __forceinline__ void load(const void *p, int64_t q, bool live)
+    {
+        raw = live ? __builtin_nontemporal_load((const u32x2 *)p + q) : u32x2{0, 0};
+    }
+    __device__ __forceinline__ float get(int k) const { return bf16_at(raw, k); }
+    __device__ __forceinline__ void store(void *p, int64_t q, const float (&nv)[4],
+                                          const bool (&keep)[4]) const
+    {
+        u32x2 o = {pack_bf16x2(nv[0], nv[1]), pack_bf16x2(nv[2], nv[3])};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t m = (keep[2 * h] ? 0x0000ffffu : 0u) | (keep[2 * h + 1] ? 0xffff0000u : 0u);
+            o[h] = (raw[h] & m) | (o[h] & ~m);
+        }
+        __builtin_nontemporal_store(o, (u32x2 *)p + q);
+    }
+};
+
 // lane ^ 16 inside each half of the wavefront (ds_swizzle bit mode: and 0x1f, xor 0x10)
 __device__ __forceinline__ float swizzle_xor16(float v)
 {
@@ -140,7 +187,7 @@ __device__ __forceinline__ float group_max4(float v)
 
 // ---------------------------------------------------------------- compress
 
-template <int BITS, int G, int MODE, int UNROLL, int MAXT>
+template <int BITS, int G, int MODE, bool SB, int UNROLL, int MAXT>
 __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTable<MAXT> tab)
 {
     constexpr int LANES = G / 4;
@@ -156,14 +203,14 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
         return;  // this tensor is smaller than the grid's widest one
     const uint16_t *__restrict__ x = rec.x;
     uint16_t *__restrict__ prev = rec.prev;
-    float *__restrict__ base = rec.base;
-    float *__restrict__ err = rec.err;
+    void *__restrict__ base = rec.base;
+    void *__restrict__ err = rec.err;
     uint8_t *__restrict__ codes = rec.codes;
     float *__restrict__ scales = rec.scales;
     const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
 
     u32x2 xv[UNROLL], pv[UNROLL];
-    f32x4 sv[UNROLL], ev[UNROLL];
+    Quad<SB> sv[UNROLL], ev[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int64_t q = q0 + (int64_t)u * kBlock;
@@ -172,9 +219,9 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
         if constexpr (USE_PREV)
             pv[u] = live ? ld_nt((const u32x2 *)(prev + 4 * q)) : u32x2{0, 0};
         if constexpr (USE_BASE)
-            sv[u] = live ? ld_nt((const f32x4 *)(base + 4 * q)) : f32x4{0, 0, 0, 0};
+            sv[u].load(base, q, live);
         if constexpr (USE_ERR)
-            ev[u] = live ? ld_nt((const f32x4 *)(err + 4 * q)) : f32x4{0, 0, 0, 0};
+            ev[u].load(err, q, live);
     }
 
 #pragma unroll
@@ -187,11 +234,11 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
         for (int k = 0; k < 4; ++k) {
             const float xk = bf16_at(xv[u], k);
             if constexpr (MODE == kDelta)
-                r[k] = (xk - bf16_at(pv[u], k)) + ev[u][k];
+                r[k] = (xk - bf16_at(pv[u], k)) + ev[u].get(k);
             else if constexpr (MODE == kLiteral)
-                r[k] = (xk - sv[u][k]) + ev[u][k];
+                r[k] = (xk - sv[u].get(k)) + ev[u].get(k);
             else
-                r[k] = xk - sv[u][k];
+                r[k] = xk - sv[u].get(k);
         }
 
         float a = fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3])));
@@ -219,28 +266,31 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
         if ((threadIdx.x & (LANES - 1)) == 0)
             scales[q / LANES] = s;
         if constexpr (USE_ERR) {
-            f32x4 n;
+            float n[4];
+            const bool none[4] = {false, false, false, false};
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 n[k] = __builtin_fmaf(-qf[k], s, r[k]);
-            st_nt(n, (f32x4 *)(err + 4 * q));
+            ev[u].store(err, q, n, none);
         }
         if constexpr (USE_PREV)
             st_nt(xv[u], (u32x2 *)(prev + 4 * q));
         if constexpr (USE_BASE) {
-            f32x4 n = sv[u];
+            float n[4];
+            bool keep[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (qf[k] != 0.0f)
-                    n[k] = __builtin_fmaf(qf[k], s, n[k]);
-            st_nt(n, (f32x4 *)(base + 4 * q));
+            for (int k = 0; k < 4; ++k) {
+                keep[k] = (qf[k] == 0.0f);
+                n[k] = __builtin_fmaf(qf[k], s, sv[u].get(k));
+            }
+            sv[u].store(base, q, n, keep);
         }
     }
 }
 
 // ---------------------------------------------------------------- decode
 
-template <int BITS, int G, int UNROLL, int MAXT>
+template <int BITS, int G, bool SB, int UNROLL, int MAXT>
 __global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MAXT> tab)
 {
     constexpr int LANES = G / 4;
@@ -250,13 +300,13 @@ __global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MA
         return;
     const uint8_t *__restrict__ codes = rec.codes;
     const float *__restrict__ scales = rec.scales;
-    float *__restrict__ base = rec.base;
+    void *__restrict__ base = rec.base;
     uint16_t *__restrict__ xhat = rec.xhat;
     const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
 
     uint32_t word[UNROLL];
     float sc[UNROLL];
-    f32x4 bv[UNROLL];
+    Quad<SB> bv[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int64_t q = q0 + (int64_t)u * kBlock;
@@ -266,32 +316,40 @@ __global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MA
         else
             word[u] = live ? (uint32_t)__builtin_nontemporal_load(codes + q) : 0u;
         sc[u] = live ? scales[q / LANES] : 0.0f;
-        bv[u] = live ? ld_nt((const f32x4 *)(base + 4 * q)) : f32x4{0, 0, 0, 0};
+        bv[u].load(base, q, live);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int64_t q = q0 + (int64_t)u * kBlock;
         if (q >= nq)
             continue;
-        f32x4 b = bv[u];
+        float n[4];
+        bool keep[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = __builtin_amdgcn_sbfe(word[u], BITS * k, BITS);  // sign-extended field
-            if (c != 0)
-                b[k] = __builtin_fmaf((float)c, sc[u], b[k]);
+            keep[k] = (c == 0);
+            n[k] = __builtin_fmaf((float)c, sc[u], bv[u].get(k));
         }
-        st_nt(b, (f32x4 *)(base + 4 * q));
-        if (xhat)
-            st_nt(u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])}, (u32x2 *)(xhat + 4 * q));
+        bv[u].store(base, q, n, keep);
+        if (xhat) {
+            float o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = keep[k] ? bv[u].get(k) : n[k];
+            st_nt(u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])}, (u32x2 *)(xhat + 4 * q));
+        }
     }
 }
 
 // ---------------------------------------------------------------- warm-up
 
 // x0 == nullptr means zeros.  Each of prev/base/err may be nullptr (not written).
+// With bf16 state the base is a copy of x0 and the error buffer bf16 zeros.
+template <bool SB>
 __global__ void __launch_bounds__(kBlock)
 cfz_warmup_kernel(const uint16_t *__restrict__ x0, uint16_t *__restrict__ prev,
-                  float *__restrict__ base, float *__restrict__ err, int64_t nchunks)
+                  void *__restrict__ base, void *__restrict__ err, int64_t nchunks)
 {
     const int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (c >= nchunks)
@@ -299,20 +357,27 @@ cfz_warmup_kernel(const uint16_t *__restrict__ x0, uint16_t *__restrict__ prev,
     const u32x4 xv = x0 ? *(const u32x4 *)(x0 + 8 * c) : u32x4{0, 0, 0, 0};
     if (prev)
         *(u32x4 *)(prev + 8 * c) = xv;
-    if (base) {
-        f32x4 b0, b1;
+    if constexpr (SB) {
+        if (base)
+            *((u32x4 *)base + c) = xv;
+        if (err)
+            *((u32x4 *)err + c) = u32x4{0, 0, 0, 0};
+    } else {
+        if (base) {
+            f32x4 b0, b1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            b0[k] = bf16_at8(xv, k);
-            b1[k] = bf16_at8(xv, k + 4);
+            for (int k = 0; k < 4; ++k) {
+                b0[k] = bf16_at8(xv, k);
+                b1[k] = bf16_at8(xv, k + 4);
+            }
+            *((f32x4 *)base + 2 * c) = b0;
+            *((f32x4 *)base + 2 * c + 1) = b1;
         }
-        *(f32x4 *)(base + 8 * c) = b0;
-        *(f32x4 *)(base + 8 * c + 4) = b1;
-    }
-    if (err) {
-        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        *(f32x4 *)(err + 8 * c) = z;
-        *(f32x4 *)(err + 8 * c + 4) = z;
+        if (err) {
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            *((f32x4 *)err + 2 * c) = z;
+            *((f32x4 *)err + 2 * c + 1) = z;
+        }
     }
 }
 
@@ -348,7 +413,7 @@ static inline unsigned grid_for(int64_t items, int64_t per_block)
 // to keep enough bytes in flight; they take four quads per lane instead.
 constexpr int64_t kBigLaunchQuads = (int64_t)4 << 20;
 
-template <int BITS, int G, int MODE, int UNROLL, int MAXT>
+template <int BITS, int G, int MODE, bool SB, int UNROLL, int MAXT>
 static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t st)
 {
     CompressTable<MAXT> tab{};
@@ -362,47 +427,47 @@ static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t 
     const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
     if (blocks > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, UNROLL, MAXT>),
+    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, SB, UNROLL, MAXT>),
                        dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
     return hipGetLastError();
 }
 
-template <int BITS, int G, int MODE>
+template <int BITS, int G, int MODE, bool SB>
 static hipError_t compress_g(const CompressItem *it, int count, int64_t total_quads, hipStream_t st)
 {
     const bool big = total_quads >= kBigLaunchQuads;
     if (count == 1)
-        return big ? compress_chunk<BITS, G, MODE, 1, 1>(it, 1, st)
-                   : compress_chunk<BITS, G, MODE, 4, 1>(it, 1, st);
-    return big ? compress_chunk<BITS, G, MODE, 1, kMaxGroup>(it, count, st)
-               : compress_chunk<BITS, G, MODE, 4, kMaxGroup>(it, count, st);
+        return big ? compress_chunk<BITS, G, MODE, SB, 1, 1>(it, 1, st)
+                   : compress_chunk<BITS, G, MODE, SB, 4, 1>(it, 1, st);
+    return big ? compress_chunk<BITS, G, MODE, SB, 1, kMaxGroup>(it, count, st)
+               : compress_chunk<BITS, G, MODE, SB, 4, kMaxGroup>(it, count, st);
 }
 
-template <int BITS, int G>
+template <int BITS, int G, bool SB>
 static hipError_t compress_m(const CompressItem *it, int count, int mode, int64_t tq, hipStream_t st)
 {
     switch (mode) {
-    case kDelta: return compress_g<BITS, G, kDelta>(it, count, tq, st);
-    case kLiteral: return compress_g<BITS, G, kLiteral>(it, count, tq, st);
-    default: return compress_g<BITS, G, kOff>(it, count, tq, st);
+    case kDelta: return compress_g<BITS, G, kDelta, SB>(it, count, tq, st);
+    case kLiteral: return compress_g<BITS, G, kLiteral, SB>(it, count, tq, st);
+    default: return compress_g<BITS, G, kOff, SB>(it, count, tq, st);
     }
 }
 
-template <int BITS>
+template <int BITS, bool SB>
 static hipError_t compress_b(const CompressItem *it, int count, int group, int mode, int64_t tq,
                              hipStream_t st)
 {
     switch (group) {
-    case 8: return compress_m<BITS, 8>(it, count, mode, tq, st);
-    case 16: return compress_m<BITS, 16>(it, count, mode, tq, st);
-    case 32: return compress_m<BITS, 32>(it, count, mode, tq, st);
-    case 64: return compress_m<BITS, 64>(it, count, mode, tq, st);
-    default: return compress_m<BITS, 128>(it, count, mode, tq, st);
+    case 8: return compress_m<BITS, 8, SB>(it, count, mode, tq, st);
+    case 16: return compress_m<BITS, 16, SB>(it, count, mode, tq, st);
+    case 32: return compress_m<BITS, 32, SB>(it, count, mode, tq, st);
+    case 64: return compress_m<BITS, 64, SB>(it, count, mode, tq, st);
+    default: return compress_m<BITS, 128, SB>(it, count, mode, tq, st);
     }
 }
 
 hipError_t launch_compress(const CompressItem *items, int count, int bits, int group, int mode,
-                           hipStream_t st)
+                           bool state_bf16, hipStream_t st)
 {
     CompressItem chunk[kMaxGroup];
     int k = 0;
@@ -413,8 +478,13 @@ hipError_t launch_compress(const CompressItem *items, int count, int bits, int g
             tq += items[i].n / 4;
         }
         if ((k == kMaxGroup || i == count) && k > 0) {
-            hipError_t e = bits == 4 ? compress_b<4>(chunk, k, group, mode, tq, st)
-                                     : compress_b<2>(chunk, k, group, mode, tq, st);
+            hipError_t e;
+            if (state_bf16)
+                e = bits == 4 ? compress_b<4, true>(chunk, k, group, mode, tq, st)
+                              : compress_b<2, true>(chunk, k, group, mode, tq, st);
+            else
+                e = bits == 4 ? compress_b<4, false>(chunk, k, group, mode, tq, st)
+                              : compress_b<2, false>(chunk, k, group, mode, tq, st);
             if (e != hipSuccess)
                 return e;
             k = 0;
@@ -424,7 +494,7 @@ hipError_t launch_compress(const CompressItem *items, int count, int bits, int g
     return hipSuccess;
 }
 
-template <int BITS, int G, int UNROLL, int MAXT>
+template <int BITS, int G, bool SB, int UNROLL, int MAXT>
 static hipError_t decode_chunk(const DecodeItem *it, int count, hipStream_t st)
 {
     DecodeTable<MAXT> tab{};
@@ -437,34 +507,36 @@ static hipError_t decode_chunk(const DecodeItem *it, int count, hipStream_t st)
     const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
     if (blocks > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, UNROLL, MAXT>),
+    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, SB, UNROLL, MAXT>),
                        dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
     return hipGetLastError();
 }
 
-template <int BITS, int G>
+template <int BITS, int G, bool SB>
 static hipError_t decode_g(const DecodeItem *it, int count, int64_t tq, hipStream_t st)
 {
     const bool big = tq >= kBigLaunchQuads;
     if (count == 1)
-        return big ? decode_chunk<BITS, G, 1, 1>(it, 1, st) : decode_chunk<BITS, G, 4, 1>(it, 1, st);
-    return big ? decode_chunk<BITS, G, 1, kMaxGroup>(it, count, st)
-               : decode_chunk<BITS, G, 4, kMaxGroup>(it, count, st);
+        return big ? decode_chunk<BITS, G, SB, 1, 1>(it, 1, st)
+                   : decode_chunk<BITS, G, SB, 4, 1>(it, 1, st);
+    return big ? decode_chunk<BITS, G, SB, 1, kMaxGroup>(it, count, st)
+               : decode_chunk<BITS, G, SB, 4, kMaxGroup>(it, count, st);
 }
 
-template <int BITS>
+template <int BITS, bool SB>
 static hipError_t decode_b(const DecodeItem *it, int count, int group, int64_t tq, hipStream_t st)
 {
     switch (group) {
-    case 8: return decode_g<BITS, 8>(it, count, tq, st);
-    case 16: return decode_g<BITS, 16>(it, count, tq, st);
-    case 32: return decode_g<BITS, 32>(it, count, tq, st);
-    case 64: return decode_g<BITS, 64>(it, count, tq, st);
-    default: return decode_g<BITS, 128>(it, count, tq, st);
+    case 8: return decode_g<BITS, 8, SB>(it, count, tq, st);
+    case 16: return decode_g<BITS, 16, SB>(it, count, tq, st);
+    case 32: return decode_g<BITS, 32, SB>(it, count, tq, st);
+    case 64: return decode_g<BITS, 64, SB>(it, count, tq, st);
+    default: return decode_g<BITS, 128, SB>(it, count, tq, st);
     }
 }
 
-hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, hipStream_t st)
+hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group, bool state_bf16,
+                         hipStream_t st)
 {
     DecodeItem chunk[kMaxGroup];
     int k = 0;
@@ -475,8 +547,13 @@ hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group
             tq += items[i].n / 4;
         }
         if ((k == kMaxGroup || i == count) && k > 0) {
-            hipError_t e = bits == 4 ? decode_b<4>(chunk, k, group, tq, st)
-                                     : decode_b<2>(chunk, k, group, tq, st);
+            hipError_t e;
+            if (state_bf16)
+                e = bits == 4 ? decode_b<4, true>(chunk, k, group, tq, st)
+                              : decode_b<2, true>(chunk, k, group, tq, st);
+            else
+                e = bits == 4 ? decode_b<4, false>(chunk, k, group, tq, st)
+                              : decode_b<2, false>(chunk, k, group, tq, st);
             if (e != hipSuccess)
                 return e;
             k = 0;
@@ -486,13 +563,17 @@ hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group
     return hipSuccess;
 }
 
-hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, float *base, float *err,
-                         int64_t nchunks, hipStream_t st)
+hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, void *base, void *err,
+                         bool state_bf16, int64_t nchunks, hipStream_t st)
 {
     if (nchunks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(cfz_warmup_kernel, dim3(grid_for(nchunks, kBlock)), dim3(kBlock), 0, st,
-                       x0, prev, base, err, nchunks);
+    if (state_bf16)
+        hipLaunchKernelGGL(cfz_warmup_kernel<true>, dim3(grid_for(nchunks, kBlock)), dim3(kBlock),
+                           0, st, x0, prev, base, err, nchunks);
+    else
+        hipLaunchKernelGGL(cfz_warmup_kernel<false>, dim3(grid_for(nchunks, kBlock)), dim3(kBlock),
+                           0, st, x0, prev, base, err, nchunks);
     return hipGetLastError();
 }
 

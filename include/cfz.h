@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CFZ_ABI_VERSION 1
+#define CFZ_ABI_VERSION 2
 
 typedef enum {
     CFZ_OK = 0,
@@ -62,35 +62,48 @@ typedef enum { CFZ_EF_DELTA = 0, CFZ_EF_LITERAL = 1, CFZ_EF_OFF = 2 } cfz_ef_mod
 
 typedef enum { CFZ_SENDER = 0, CFZ_RECEIVER = 1 } cfz_role;
 
+/* Precision of the carried error E and of the base X-hat.
+ *   F32:  fp32 state (default).
+ *   BF16: bf16 state, half the state traffic.  Every update is the same fp32
+ *         fma as with F32, rounded once to bf16 (nearest even); a zero code
+ *         leaves the base's bits untouched.  In OFF mode sender and receiver
+ *         then hold bit-identical bf16 bases and the closed loop absorbs the
+ *         rounding; the receiver's base is directly a bf16 activation. */
+typedef enum { CFZ_STATE_F32 = 0, CFZ_STATE_BF16 = 1 } cfz_state_dtype;
+
 /* One exchanged tensor: rows (tokens) x cols (channels), quantized in groups of
  * `group` consecutive channels of one row with `bits`-bit codes.
  * Requirements: rows >= 0, cols >= 0, bits in {2, 4}, group in {8,16,32,64,128},
- * cols % group == 0.  rows * cols == 0 is allowed (every call is then a no-op). */
+ * cols % group == 0, state_dtype a cfz_state_dtype, reserved == 0.
+ * rows * cols == 0 is allowed (every call is then a no-op). */
 typedef struct {
     int64_t rows;
     int64_t cols;
     int32_t bits;
     int32_t group;
-    int32_t ef_mode; /* cfz_ef_mode */
-    int32_t role;    /* cfz_role    */
+    int32_t ef_mode;     /* cfz_ef_mode     */
+    int32_t role;        /* cfz_role        */
+    int32_t state_dtype; /* cfz_state_dtype */
+    int32_t reserved;    /* must be 0       */
 } cfz_desc;
 
 /* Caller-owned state buffers, rows*cols elements each, on the device.
  *   prev_bf16: sender in DELTA mode (previous activation, bf16).
- *   base_f32:  receiver; sender in LITERAL and OFF modes (running reconstruction).
- *   err_f32:   sender in DELTA and LITERAL modes (carried error).
+ *   base:      receiver; sender in LITERAL and OFF modes (running reconstruction).
+ *   err:       sender in DELTA and LITERAL modes (carried error).
+ * base and err hold fp32 or bf16 values according to desc.state_dtype.
  * Buffers the role/mode does not use are ignored and may be NULL. */
 typedef struct {
     uint16_t *prev_bf16;
-    float *base_f32;
-    float *err_f32;
+    void *base;
+    void *err;
 } cfz_buffers;
 
 typedef struct cfz_state cfz_state;
 
 /* Warm-up (step 0): the uncompressed activation x0 initialises the state.
- * Receiver: base = fp32(x0).  Sender: prev = x0 (DELTA), base = fp32(x0)
- * (LITERAL, OFF), err = 0 (DELTA, LITERAL).  x0 == NULL means all zeros.
+ * Receiver: base = x0.  Sender: prev = x0 (DELTA), base = x0 (LITERAL, OFF),
+ * err = 0 (DELTA, LITERAL) -- in the state's precision (bf16 to fp32 is exact).  x0 == NULL means all zeros.
  * Enqueues one initialisation kernel on hip_stream, then returns the handle.
  * On error *out is left unchanged.  (paper: reproducibility table,
  * "Dataset Splits" -- warm-up initialises the base tensor.) */
@@ -127,8 +140,9 @@ cfz_status cfz_compress(cfz_state *sender, const uint16_t *x_bf16, uint8_t *code
                         float *scales, void *hip_stream);
 
 /* One step at the receiver: unpack, sign-extend, base' = fma(q, s, base) where
- * q != 0 (a zero code leaves the base bit-identical), and optionally write the
- * new base rounded to bf16 (nearest even) into xhat_bf16 (may be NULL).
+ * q != 0 (a zero code leaves the base bit-identical; with bf16 state the fma
+ * result is rounded once to bf16), and optionally write the new base rounded to
+ * bf16 (nearest even) into xhat_bf16 (may be NULL).
  * Errors: CFZ_ERR_NULL, CFZ_ERR_ALIGN, CFZ_ERR_MODE (sender state), CFZ_ERR_HIP. */
 cfz_status cfz_decompress(cfz_state *receiver, const uint8_t *codes, const float *scales,
                           uint16_t *xhat_bf16, void *hip_stream);

@@ -17,7 +17,7 @@ def test_library_exports_every_declared_function():
     assert len(names) == 16
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
-    assert cfz.cfz_abi_version() == 1
+    assert cfz.cfz_abi_version() == 2
 
 
 def test_status_strings():
@@ -54,6 +54,8 @@ def _create_status(desc, bufs, x0=None):
     (cfz.make_desc(4, 96, group=64), cfz.CFZ_ERR_SHAPE),
     (cfz.make_desc(4, 64, ef_mode=3), cfz.CFZ_ERR_MODE),
     (cfz.make_desc(4, 64, role=2), cfz.CFZ_ERR_MODE),
+    (cfz.make_desc(4, 64, state_dtype=2), cfz.CFZ_ERR_UNSUPPORTED),
+    (cfz.cfz_desc(4, 64, 4, 64, 0, 0, 0, 1), cfz.CFZ_ERR_SHAPE),  # reserved must be 0
 ])
 def test_create_rejects_bad_descriptor(desc, status):
     bufs = cfz.cfz_buffers(ALIGNED, ALIGNED, ALIGNED)
@@ -154,6 +156,8 @@ def test_group_validation_without_launching():
     lit = cfz.cfz_state_resume(cfz.make_desc(4, 64, ef_mode=cfz.CFZ_EF_LITERAL), base=ALIGNED,
                                err=ALIGNED)
     rcv = cfz.cfz_state_resume(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER), base=ALIGNED)
+    half = cfz.cfz_state_resume(cfz.make_desc(4, 64, state_dtype=cfz.CFZ_STATE_BF16),
+                                prev=ALIGNED, err=ALIGNED)
     P = C.c_void_p
 
     def arr(*v):
@@ -169,6 +173,10 @@ def test_group_validation_without_launching():
                                       arr(ALIGNED, ALIGNED), None) == cfz.CFZ_ERR_MODE
         assert lib.cfz_compress_group(2, arr(a, a), arr(ALIGNED, ALIGNED), arr(ALIGNED, ALIGNED),
                                       arr(ALIGNED, ALIGNED), None) == cfz.CFZ_ERR_MODE
+        # fp32 and bf16 state cannot share one launch
+        assert lib.cfz_compress_group(2, arr(a, half), arr(ALIGNED, ALIGNED),
+                                      arr(ALIGNED, ALIGNED), arr(ALIGNED, ALIGNED),
+                                      None) == cfz.CFZ_ERR_MODE
         assert lib.cfz_compress_group(1, arr(rcv), arr(ALIGNED), arr(ALIGNED), arr(ALIGNED),
                                       None) == cfz.CFZ_ERR_MODE
         st = lib.cfz_compress_group(2, arr(a, b), arr(ALIGNED, ALIGNED), arr(ALIGNED, MISALIGNED),
@@ -180,5 +188,5 @@ def test_group_validation_without_launching():
                                         None) == cfz.CFZ_ERR_ALIGN
         assert cfz.cfz_state_steps(a) == 0 and cfz.cfz_state_steps(b) == 0
     finally:
-        for h in (a, b, lit, rcv):
+        for h in (a, b, lit, rcv, half):
             cfz.cfz_state_destroy(h)

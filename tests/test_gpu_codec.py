@@ -2,7 +2,8 @@
 
 Bar: packed codes and fp32 scales bit-exact; error buffer, previous activation,
 bases and bf16 reconstructions bit-exact as well (both sides use IEEE fp32
-division, ties-to-even rounding and the same two explicit fma operations).
+division, ties-to-even rounding and the same two explicit fma operations; with
+bf16 state each fma result is rounded once to bf16, ties to even).
 Inputs: seeded AR(1) activations at the workload shapes (synth module)."""
 import ctypes as C
 import sys
@@ -35,6 +36,16 @@ def u32(t):
     return t.contiguous().cpu().numpy().view(np.uint32).reshape(-1)
 
 
+def sbits(t):
+    """Bit patterns of a state tensor, fp32 or bf16."""
+    return u16(t) if t.element_size() == 2 else u32(t)
+
+
+def obits(a):
+    """Bit patterns of an oracle state array (uint16 for bf16 state, else fp32)."""
+    return a if a.dtype == np.uint16 else a.view(np.uint32)
+
+
 @pytest.fixture(autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
@@ -45,24 +56,26 @@ def _compare_step(tag, gs, gr, codes, scales, os_, or_, ocodes, oscales, xhat=No
     assert np.array_equal(codes.cpu().numpy(), ocodes), f"{tag}: codes"
     assert np.array_equal(u32(scales), oscales.view(np.uint32)), f"{tag}: scales"
     if os_.err is not None:
-        assert np.array_equal(u32(gs.err), os_.err.view(np.uint32)), f"{tag}: err"
+        assert np.array_equal(sbits(gs.err), obits(os_.err)), f"{tag}: err"
     if os_.prev is not None:
         assert np.array_equal(u16(gs.prev), os_.prev), f"{tag}: prev"
     if os_.base is not None:
-        assert np.array_equal(u32(gs.base), os_.base.view(np.uint32)), f"{tag}: sender base"
-    assert np.array_equal(u32(gr.base), or_.base.view(np.uint32)), f"{tag}: receiver base"
+        assert np.array_equal(sbits(gs.base), obits(os_.base)), f"{tag}: sender base"
+    assert np.array_equal(sbits(gr.base), obits(or_.base)), f"{tag}: receiver base"
     if xhat is not None:
         assert np.array_equal(u16(xhat), oxhat), f"{tag}: xhat"
 
 
-def _run_parity(xs, rows, cols, bits, group, mode, tag, want_xhat=True):
+def _run_parity(xs, rows, cols, bits, group, mode, tag, want_xhat=True, state_bf16=False):
     """xs: list of bf16 CPU tensors [rows, cols]; step 0 is the warm-up."""
     n = rows * cols
-    say(f"[gpu] {tag}: rows={rows} cols={cols} bits={bits} group={group} mode={mode}")
-    gs = cfz.Sender(rows, cols, bits, group, mode, x0=xs[0].to(DEV))
-    gr = cfz.Receiver(rows, cols, bits, group, x0=xs[0].to(DEV))
-    os_ = oracle.Sender(n, bits, group, MODE_PAIRS[mode], x0=u16(xs[0]))
-    or_ = oracle.Receiver(n, bits, group, x0=u16(xs[0]))
+    say(f"[gpu] {tag}: rows={rows} cols={cols} bits={bits} group={group} mode={mode} "
+        f"bf16 state={state_bf16}")
+    sb = state_bf16
+    gs = cfz.Sender(rows, cols, bits, group, mode, x0=xs[0].to(DEV), state_bf16=sb)
+    gr = cfz.Receiver(rows, cols, bits, group, x0=xs[0].to(DEV), state_bf16=sb)
+    os_ = oracle.Sender(n, bits, group, MODE_PAIRS[mode], x0=u16(xs[0]), state_bf16=sb)
+    or_ = oracle.Receiver(n, bits, group, x0=u16(xs[0]), state_bf16=sb)
     xhat = torch.empty(n, dtype=torch.bfloat16, device=DEV) if want_xhat else None
     for t in range(1, len(xs)):
         codes, scales = gs.compress(xs[t].to(DEV))
@@ -119,10 +132,8 @@ def test_empty_tensor_is_a_noop():
     assert codes.numel() == 0 and scales.numel() == 0
 
 
-def test_extreme_magnitudes():
-    """Subnormal, tiny and huge groups, all-zero groups and exact ties."""
+def _extreme_inputs(rows=64, cols=512):
     rng = np.random.default_rng(5)
-    rows, cols = 64, 512
     mags = np.array([1e-38, 1e-30, 3e-39, 1.0, 1e20, 1e30, 0.0, 1e-3], np.float32)
     sc = np.repeat(mags, cols // len(mags))
     xs = []
@@ -132,23 +143,60 @@ def test_extreme_magnitudes():
             v[:8] = np.round(rng.uniform(-7, 7, (8, cols)) * 2) / 2  # half-integer lattice
         xs.append(torch.from_numpy(v).to(torch.bfloat16))
     xs[3][10:20] = xs[2][10:20]  # unchanged rows: zero residual in DELTA
+    return xs
+
+
+@pytest.mark.parametrize("state_bf16", [False, True])
+def test_extreme_magnitudes(state_bf16):
+    """Subnormal, tiny and huge groups, all-zero groups and exact ties."""
+    xs = _extreme_inputs()
     for bits, group in ((4, 64), (2, 32), (4, 8)):
         for mode in (0, 1, 2):
-            _run_parity(xs, rows, cols, bits, group, mode, f"extreme b{bits} g{group} m{mode}")
+            _run_parity(xs, 64, 512, bits, group, mode, f"extreme b{bits} g{group} m{mode}",
+                        state_bf16=state_bf16)
 
 
-def test_zero_residual_leaves_state_bitwise():
-    say("[gpu] zero residual")
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", [8, 32, 128])
+@pytest.mark.parametrize("bits", [4, 2])
+def test_bf16_state_several_tiles_and_ragged_tail(bits, group, mode):
+    """Carried error and base kept in bf16: every state update rounded once to bf16."""
+    xs = [x[0] for x in _ar1(300, 256, 5, seed=7 * bits + group + mode)]
+    _run_parity(xs, 300, 256, bits, group, mode, f"bf16 state b{bits} g{group} m{mode}",
+                state_bf16=True)
+
+
+def test_bf16_state_odd_shapes_and_empty():
+    for rows, cols, group in ((1, 8, 8), (5, 24, 8), (513, 64, 32)):
+        xs = [x[0] for x in _ar1(rows, cols, 3, seed=rows * cols)]
+        _run_parity(xs, rows, cols, 4, group, cfz.CFZ_EF_DELTA, f"bf16 state {rows}x{cols}",
+                    state_bf16=True)
+    s = cfz.Sender(0, 64, 4, 64, state_bf16=True)
+    r = cfz.Receiver(0, 64, 4, 64, state_bf16=True)
+    codes, scales = s.compress(torch.empty(0, dtype=torch.bfloat16, device=DEV))
+    r.decompress(codes, scales)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("state_bf16", [False, True])
+def test_zero_residual_leaves_state_bitwise(state_bf16):
+    say(f"[gpu] zero residual, bf16 state={state_bf16}")
     x0 = _ar1(64, 256, 1)[0][0].to(DEV)
-    s = cfz.Sender(64, 256, 4, 64, cfz.CFZ_EF_DELTA, x0=x0)
-    r = cfz.Receiver(64, 256, 4, 64, x0=x0)
+    s = cfz.Sender(64, 256, 4, 64, cfz.CFZ_EF_DELTA, x0=x0, state_bf16=state_bf16)
+    r = cfz.Receiver(64, 256, 4, 64, x0=x0, state_bf16=state_bf16)
     base0 = r.base.clone()
     codes, scales = s.compress(x0)
     r.decompress(codes, scales)
     torch.cuda.synchronize()
     assert not codes.any() and not scales.any()
-    assert not s.err.view(torch.int32).any()
-    assert torch.equal(r.base.view(torch.int32), base0.view(torch.int32))
+    assert not s.err.view(torch.int16 if state_bf16 else torch.int32).any()
+    assert torch.equal(sbits_t(r.base), sbits_t(base0))
+    if state_bf16:  # the warm-up base of a bf16 receiver is x0 itself
+        assert torch.equal(r.base.view(torch.int16), x0.reshape(-1).view(torch.int16))
+
+
+def sbits_t(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
 
 
 def test_checkpoint_resume_and_determinism():
@@ -230,20 +278,23 @@ def test_runs_on_a_side_stream():
 
 # ------------------------------------------------------------------ full workload sizes
 
-def test_flux_int4_full_size_sampled_tensors():
+@pytest.mark.parametrize("state_bf16", [False, True])
+def test_flux_int4_full_size_sampled_tensors(state_bf16):
     """FLUX.1-dev share, 57 layers x {K, V} of 1024 x 3072, int4 g64, DELTA, 28 steps, in the
     launch configuration of the benchmark (one grouped launch per layer for its K and V);
     layers 0, 28 and 56 are compared every step."""
     sp = SPECS["flux"]
     st = AR1Stream.from_spec(sp, seed=0, device=DEV)
     picks = [0, 1, 56, 57, 112, 113]
-    say(f"[gpu] flux int4 full size, tensors {picks}")
+    say(f"[gpu] flux int4 full size, tensors {picks}, bf16 state={state_bf16}")
     x = st.next()
     n = sp.rows * sp.cols
-    gs = [cfz.Sender(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous()) for i in picks]
-    gr = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous()) for i in picks]
-    os_ = [oracle.Sender(n, 4, 64, oracle.DELTA, x0=u16(x[i])) for i in picks]
-    or_ = [oracle.Receiver(n, 4, 64, x0=u16(x[i])) for i in picks]
+    sb = state_bf16
+    gs = [cfz.Sender(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous(), state_bf16=sb) for i in picks]
+    gr = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x[i].contiguous(), state_bf16=sb)
+          for i in picks]
+    os_ = [oracle.Sender(n, 4, 64, oracle.DELTA, x0=u16(x[i]), state_bf16=sb) for i in picks]
+    or_ = [oracle.Receiver(n, 4, 64, x0=u16(x[i]), state_bf16=sb) for i in picks]
     for t in range(1, sp.steps):
         x = st.next()
         for j in range(0, len(picks), 2):  # K and V of one layer per grouped call
@@ -339,22 +390,25 @@ def test_graph_replay_matches_oracle_every_replay():
         _compare_step(f"graph replay {t}", gs, gr, gs.codes, gs.scales, os_, or_, oc, osc)
 
 
-@pytest.mark.parametrize("bits,group,mode", [(4, 64, 0), (2, 32, 0), (4, 128, 1), (2, 8, 2)])
-def test_grouped_launch_matches_oracle(bits, group, mode):
+@pytest.mark.parametrize("bits,group,mode,sb", [(4, 64, 0, False), (2, 32, 0, False),
+                                                (4, 128, 1, False), (2, 8, 2, False),
+                                                (4, 64, 0, True), (2, 16, 2, True)])
+def test_grouped_launch_matches_oracle(bits, group, mode, sb):
     """Separately allocated tensors of different sizes (one empty) in grouped calls: more than
     16 tensors, so the call spans several launches, and both launch shapes (big and small)."""
     shapes = [(1024, 1024)] * 17 + [(300, 256), (0, 256), (17, 128), (64, 1024)]
-    say(f"[gpu] grouped b{bits} g{group} m{mode}: {len(shapes)} tensors")
+    say(f"[gpu] grouped b{bits} g{group} m{mode} bf16 state={sb}: {len(shapes)} tensors")
     seqs = [[x[0] for x in _ar1(r, c, 4, seed=100 + i)] if r else None
             for i, (r, c) in enumerate(shapes)]
     snd, rcv, osnd, orcv, xh = [], [], [], [], []
     for i, (r, c) in enumerate(shapes):
         x0 = seqs[i][0].to(DEV) if r else None
-        snd.append(cfz.Sender(r, c, bits, group, mode, x0=x0))
-        rcv.append(cfz.Receiver(r, c, bits, group, x0=x0))
+        snd.append(cfz.Sender(r, c, bits, group, mode, x0=x0, state_bf16=sb))
+        rcv.append(cfz.Receiver(r, c, bits, group, x0=x0, state_bf16=sb))
         osnd.append(oracle.Sender(r * c, bits, group, MODE_PAIRS[mode],
-                                  x0=u16(seqs[i][0]) if r else None))
-        orcv.append(oracle.Receiver(r * c, bits, group, x0=u16(seqs[i][0]) if r else None))
+                                  x0=u16(seqs[i][0]) if r else None, state_bf16=sb))
+        orcv.append(oracle.Receiver(r * c, bits, group, x0=u16(seqs[i][0]) if r else None,
+                                    state_bf16=sb))
         xh.append(torch.empty(r * c, dtype=torch.bfloat16, device=DEV))
     for t in range(1, 4):
         xs = [seqs[i][t].to(DEV) if r else torch.empty(0, dtype=torch.bfloat16, device=DEV)
