@@ -365,9 +365,12 @@ def main():
         pe = n * T / r_["launches"]
         c16 = bc16 * pe / (r_["t_comp"] / nl) / 1e9
         d16 = bd16 * pe / (r_["t_dec"] / nl) / 1e9
+        wl16 = f"flux-share-57x2x1024x3072-int4-g64-delta-bf16state/{args.launch}"
         bf16_state = {
             "workload": f"{T} tensors of {rows}x{cols}, int{bits} g{group}, delta, carried "
                         "error and base in bf16", "steps": kb,
+            "traffic_bytes_per_launch": {"compress": load_traffic("compress_bf16_state", wl16),
+                                         "decode": load_traffic("decode_bf16_state", wl16)},
             "activation_GB/s": round(2 * n * T * kb / r_["elapsed"] / 1e9, 2),
             "compress": {"avg_launch_us": round(r_["t_comp"] / nl * 1e6, 3),
                          "GB/s": round(c16, 1), "frac_hbm_peak": round(c16 / HBM_PEAK_GBS, 4),
