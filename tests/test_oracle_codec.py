@@ -437,3 +437,47 @@ def test_bf16_state_accuracy_matches_fp32_state(mode):
         return np.linalg.norm(xt - b) / np.linalg.norm(xt)
     e32, e16 = final_err(False), final_err(True)
     assert abs(e16 - e32) <= 0.05 * e32
+
+
+def _rne_bf16_numpy(f32):
+    """fp32 -> bf16 bits, round to nearest even, written with integer ops (finite inputs)."""
+    u = np.ascontiguousarray(f32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("mode", [oracle.DELTA, oracle.LITERAL, oracle.OFF])
+@pytest.mark.parametrize("bits,group", [(4, 64), (2, 8)])
+def test_bf16_state_step_is_fp32_step_rounded(mode, bits, group):
+    """From a state that is exact in bf16, one bf16-state step gives the same codes and scales
+    as the fp32-state step, and each state array equals the fp32 result rounded to bf16."""
+    rng = np.random.default_rng(11 + mode + bits)
+    n = 2048
+    x = oracle.f32_to_bf16(rng.standard_normal(n).astype(np.float32))
+    p = oracle.f32_to_bf16(rng.standard_normal(n).astype(np.float32))
+    e16 = _rne_bf16_numpy((rng.standard_normal(n) * 0.05).astype(np.float32))
+    b16 = _rne_bf16_numpy(rng.standard_normal(n).astype(np.float32))
+    b16[::7] = x[::7]                       # some zero residuals in OFF mode
+    widen = lambda h: (h.astype(np.uint32) << 16).view(np.float32)
+    s32 = oracle.Sender(n, bits, group, mode)
+    s16 = oracle.Sender(n, bits, group, mode, state_bf16=True)
+    for s_, e_, b_ in ((s32, widen(e16), widen(b16)), (s16, e16, b16)):
+        if s_.prev is not None:
+            s_.prev[:] = p
+        if s_.err is not None:
+            s_.err[:] = e_
+        if s_.base is not None:
+            s_.base[:] = b_
+    c32, sc32 = s32.compress(x)
+    c16, sc16 = s16.compress(x)
+    assert np.array_equal(c32, c16) and np.array_equal(sc32.view(np.uint32), sc16.view(np.uint32))
+    for a32, a16 in ((s32.err, s16.err), (s32.base, s16.base)):
+        if a32 is not None:
+            assert np.array_equal(_rne_bf16_numpy(a32), a16)
+    # receiver: one decode from the same bf16-exact base
+    r32 = oracle.Receiver(n, bits, group)
+    r16 = oracle.Receiver(n, bits, group, state_bf16=True)
+    r32.base[:] = widen(b16)
+    r16.base[:] = b16
+    r32.decompress(c32, sc32)
+    r16.decompress(c32, sc32)
+    assert np.array_equal(_rne_bf16_numpy(r32.base), r16.base)
