@@ -42,6 +42,9 @@ def _load():
     lib.oracle_qr.argtypes = [i64, i32, p, p, p]
     lib.oracle_qr.restype = i32
     lib.oracle_lowrank.argtypes = [i64, i64, i32, i32, p, p, p, p, p]
+    lib.oracle_lowrank_ef_update.argtypes = [i64, i64, i32, p, p, p, C.c_double, p]
+    lib.oracle_lowrank_ef_compress.argtypes = [i64, i64, i32, i32, p, p, p, p, p, p, p, p]
+    lib.oracle_lowrank_ef_decompress.argtypes = [i64, i64, i32, p, p, p, p, p]
     lib.oracle_qmax.argtypes = [i32]
     lib.oracle_qmax.restype = i32
     _lib = lib
@@ -185,3 +188,64 @@ def lowrank(A_bf16: np.ndarray, Q0: np.ndarray, T: int):
     RU = np.zeros((r, r), np.float64)
     _load().oracle_lowrank(m, n, r, T, _ptr(A_bf16), _ptr(Q0), _ptr(U), _ptr(V), _ptr(RU))
     return U, V, RU
+
+
+# ---------------------------------------------------------------- low rank inside error feedback
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def lowrank_ef_update(U, V, RU, sign, Y):
+    """Y (m x n fp32, in place) += sign * (U R_U) V^T, each element rounded once from fp64."""
+    U, V, RU = _f64(U), _f64(V), _f64(RU)
+    m, r = U.shape
+    n = V.shape[0]
+    assert Y.dtype == np.float32 and Y.size == m * n and Y.flags["C_CONTIGUOUS"]
+    _load().oracle_lowrank_ef_update(m, n, r, _ptr(U), _ptr(V), _ptr(RU), float(sign), _ptr(Y))
+    return Y
+
+
+class LowrankSender:
+    """Sender state of the rank-r compressor inside error feedback: prev (bf16 bits) and the
+    fp32 carried error, warmed up like the quantizer's DELTA mode."""
+
+    def __init__(self, m, n, x0=None):
+        self.m, self.n = m, n
+        self.prev = np.zeros(m * n, np.uint16)
+        self.err = np.zeros(m * n, np.float32)
+        if x0 is not None:
+            self.prev[:] = np.ascontiguousarray(x0, np.uint16).reshape(-1)
+
+    def compress(self, x, Q0, T):
+        """One step: returns (U, V, RU) in fp64 and A, the bf16 residual that was compressed."""
+        x = np.ascontiguousarray(x, np.uint16).reshape(-1)
+        Q0 = np.ascontiguousarray(Q0, np.float32)
+        r = Q0.shape[1]
+        assert x.size == self.m * self.n and Q0.shape[0] == self.n
+        A = np.zeros(self.m * self.n, np.uint16)
+        U = np.zeros((self.m, r), np.float64)
+        V = np.zeros((self.n, r), np.float64)
+        RU = np.zeros((r, r), np.float64)
+        _load().oracle_lowrank_ef_compress(self.m, self.n, r, T, _ptr(x), _ptr(self.prev),
+                                           _ptr(self.err), _ptr(Q0), _ptr(A), _ptr(U), _ptr(V),
+                                           _ptr(RU))
+        return U, V, RU, A
+
+
+class LowrankReceiver:
+    """Receiver state: the fp32 base, warmed up to x0."""
+
+    def __init__(self, m, n, x0=None):
+        self.m, self.n = m, n
+        self.base = np.zeros(m * n, np.float32)
+        if x0 is not None:
+            self.base[:] = bf16_to_f32(np.ascontiguousarray(x0, np.uint16).reshape(-1))
+
+    def decompress(self, U, V, RU, want_xhat=False):
+        U, V, RU = _f64(U), _f64(V), _f64(RU)
+        r = U.shape[1]
+        xhat = np.zeros(self.m * self.n, np.uint16) if want_xhat else None
+        _load().oracle_lowrank_ef_decompress(self.m, self.n, r, _ptr(U), _ptr(V), _ptr(RU),
+                                             _ptr(self.base), _ptr(xhat))
+        return xhat

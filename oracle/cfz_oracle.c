@@ -42,7 +42,10 @@
  *     reconstruction is U R_U V^T = (A Q) Q^T;
  *   - optional bf16 state: the carried error and the base are stored in bf16;
  *     each update is the same fp32 fmaf, rounded once to bf16 (nearest even),
- *     and a zero code still leaves the base untouched.
+ *     and a zero code still leaves the base untouched;
+ *   - the rank-r compressor inside the error-feedback loop: the DELTA residual
+ *     rounded to bf16 goes through Algorithm 3, and the carried error and the
+ *     receiver's base are updated with the fp64 reconstruction U R_U V^T.
  *
  * Parity of every function here is pinned by the CPU tests (closed forms,
  * hand-derived fixtures, brute force, invariants, exact-rank recovery and the
@@ -414,4 +417,73 @@ void oracle_lowrank(int64_t m, int64_t n, int r, int T, const uint16_t *A_bf16,
     free(A);
 }
 
-int oracle_abi_version(void) { return 1; }
+/* ------------------------------------------------------------------ */
+/* The rank-r compressor inside the error-feedback loop.  The pages give
+ * error feedback on step-wise differences as the method and the subspace
+ * iteration (Algorithm 3) as a compressor; they are combined here the way the
+ * quantizer is used: the DELTA-mode residual is rounded to bf16 (the input
+ * type of the subspace iteration), compressed to (U, R_U, V), and what the
+ * reconstruction misses is carried to the next step.
+ *
+ * Sender, one step, for one m x n tensor:
+ *   r = (x - prev) + err          fp32, as in the quantizer's DELTA mode
+ *   A = bf16(r)                   round to nearest even
+ *   (U, V, R_U) = Algorithm 3 on A with the random sample Q0
+ *   D = (U R_U) V^T               fp64
+ *   err' = fp32(r - D), prev' = x
+ * Receiver: base' = fp32(base + D), xhat = bf16(base').
+ * The warm-up is the quantizer's DELTA warm-up (prev = x0, err = 0; base = x0).
+ * Plain additions: a zero D leaves every value unchanged (a -0 base may become
+ * +0). */
+
+/* Y = fp32(Y + sign * (U R_U) V^T), every element from its fp64 sum. */
+void oracle_lowrank_ef_update(int64_t m, int64_t n, int r, const double *U, const double *V,
+                              const double *RU, double sign, float *Y)
+{
+    double *W = (double *)malloc(sizeof(double) * (size_t)(m * r));
+    for (int64_t i = 0; i < m; ++i)
+        for (int k = 0; k < r; ++k) {
+            double acc = 0.0;
+            for (int l = 0; l < r; ++l)
+                acc += U[i * r + l] * RU[l * r + k];
+            W[i * r + k] = acc;
+        }
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double d = 0.0;
+            for (int k = 0; k < r; ++k)
+                d += W[i * r + k] * V[j * r + k];
+            Y[i * n + j] = (float)((double)Y[i * n + j] + sign * d);
+        }
+    free(W);
+}
+
+/* Sender step.  A (m x n bf16, the compressed residual) may be NULL. */
+void oracle_lowrank_ef_compress(int64_t m, int64_t n, int r, int T, const uint16_t *x,
+                                uint16_t *prev, float *err, const float *Q0, uint16_t *A,
+                                double *U, double *V, double *RU)
+{
+    uint16_t *a = A ? A : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(m * n));
+    for (int64_t j = 0; j < m * n; ++j) {
+        float rj = (bf16_to_float(x[j]) - bf16_to_float(prev[j])) + err[j];
+        err[j] = rj;
+        a[j] = float_to_bf16(rj);
+        prev[j] = x[j];
+    }
+    oracle_lowrank(m, n, r, T, a, Q0, U, V, RU);
+    oracle_lowrank_ef_update(m, n, r, U, V, RU, -1.0, err);
+    if (!A)
+        free(a);
+}
+
+/* Receiver step.  xhat (bf16 copy of the new base) may be NULL. */
+void oracle_lowrank_ef_decompress(int64_t m, int64_t n, int r, const double *U, const double *V,
+                                  const double *RU, float *base, uint16_t *xhat)
+{
+    oracle_lowrank_ef_update(m, n, r, U, V, RU, 1.0, base);
+    if (xhat)
+        for (int64_t j = 0; j < m * n; ++j)
+            xhat[j] = float_to_bf16(base[j]);
+}
+
+int oracle_abi_version(void) { return 2; }

@@ -24,6 +24,7 @@ drawn here so that every implementation sees identical bits).
 from __future__ import annotations
 
 import hashlib
+import math
 from dataclasses import dataclass
 
 import torch
@@ -151,3 +152,33 @@ def exact_rank_batch(batch, m, n, rank, seed=0, key="exact", device="cpu"):
     gg = torch.randint(-1, 2, (batch, n, rank), generator=g).to(torch.float64)
     a = torch.bmm(f, gg.transpose(1, 2).contiguous())
     return a.to(torch.bfloat16).to(device)
+
+
+class LowrankDrift:
+    """Activations whose step-to-step change is low-rank plus noise, ``[batch, rows, cols]`` bf16.
+
+    X_0 = N(0, 1); X_t = X_{t-1} + c * (F_t G_t^T / sqrt(rank) + sigma * N(0, 1)) with F_t
+    (rows x rank) and G_t (cols x rank) Gaussian, drawn afresh every step.  The generator keeps
+    X in fp32 and emits it rounded to bf16.  The first call of ``next`` returns X_0."""
+
+    def __init__(self, batch, rows, cols, rank=16, sigma=0.05, c=0.2, seed=0, key="lrdrift",
+                 device="cpu"):
+        self.batch, self.rows, self.cols = batch, rows, cols
+        self.rank, self.sigma, self.c = rank, sigma, c
+        self.device = device
+        self.g = torch.Generator(device=device)
+        self.g.manual_seed(seed_for(seed, key, batch, rows, cols, rank))
+        self.x = None
+
+    def next(self) -> torch.Tensor:
+        shape = (self.batch, self.rows, self.cols)
+        if self.x is None:
+            self.x = torch.randn(shape, generator=self.g, device=self.device)
+        else:
+            f = torch.randn((self.batch, self.rows, self.rank), generator=self.g, device=self.device)
+            gg = torch.randn((self.batch, self.cols, self.rank), generator=self.g,
+                             device=self.device)
+            inc = torch.bmm(f, gg.transpose(1, 2).contiguous()) / math.sqrt(self.rank)
+            inc += self.sigma * torch.randn(shape, generator=self.g, device=self.device)
+            self.x += self.c * inc
+        return self.x.to(torch.bfloat16)
