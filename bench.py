@@ -164,6 +164,44 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
     return out
 
 
+def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps=6, pool=4):
+    """The rank-r compressor inside error feedback on 57 layers of 1024 x 3072 per step:
+    activations drift by rank 16 + noise per step.  One step = one sender call (residual,
+    subspace iteration, error update) and one receiver call (base update + bf16 output)."""
+    from synth import LowrankDrift, gaussian_q0
+
+    st = LowrankDrift(batch, m, n, rank=16, seed=3, device=dev)
+    X = [st.next() for _ in range(pool + 1)]
+    del st
+    Q0 = [gaussian_q0(batch, n, r, seed=s, device=dev) for s in range(pool)]
+    snd = cfz.LowrankSender(batch, m, n, r, x0=X[0])
+    rcv = cfz.LowrankReceiver(batch, m, n, r, x0=X[0])
+    xhat = torch.empty(batch * m * n, dtype=torch.bfloat16, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
+    for k in range(steps + 1):  # the first step is an untimed warm-up
+        ev[k][0].record()
+        snd.compress(X[1 + k % pool], Q0[k % pool], T)
+        ev[k][1].record()
+        rcv.decompress(snd.U, snd.V, snd.RU, xhat)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / steps
+    td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / steps
+    elems = batch * m * n
+    payload = batch * 4 * (m * r + r * r + n * r)
+    upd_bytes = 10 * elems  # read + write fp32 base, write bf16 xhat
+    del snd, rcv, X, Q0, xhat
+    return {"workload": f"{batch} x {m}x{n}, activations drifting by rank 16 + 0.05 noise, "
+                        f"r={r}, T={T}, random Q0 each step", "steps": steps,
+            "activation_GB/s": round(2 * elems / (tc + td) / 1e9, 2),
+            "compress_ms": round(tc * 1e3, 4), "decompress_ms": round(td * 1e3, 4),
+            "compression_ratio_vs_bf16": round(2 * elems / payload, 1),
+            "decompress_update_kernel": {
+                "GB/s": round(upd_bytes / td / 1e9, 1),
+                "frac_hbm_peak": round(upd_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_elem": 10}}
+
+
 def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
     """The fp64 CPU oracle on one layer per rank; per-call figures scale that by the batch."""
     import numpy as np
@@ -446,6 +484,8 @@ def main():
             print("[bench] CPU oracle baseline (subspace iteration)", file=sys.stderr, flush=True)
             lr["cpu_baseline"] = lowrank_cpu_baseline(a0, 57)
         line["lowrank"] = lr
+        print("[bench] low-rank inside error feedback leg", file=sys.stderr, flush=True)
+        line["lowrank_ef"] = bench_lowrank_ef(cfz, torch, dev)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         sample_tensors = 114

@@ -65,6 +65,10 @@ def _load():
         "cfz_decompress_group": ([i32, p, p, p, p, p], i32),
         "cfz_lowrank_workspace_bytes": ([i64, i64, i64, i32], sz),
         "cfz_lowrank": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, sz, p], i32),
+        "cfz_lowrank_ef_workspace_bytes": ([i64, i64, i64, i32], sz),
+        "cfz_lowrank_ef_warmup": ([i64, p, p, p, p, p], i32),
+        "cfz_lowrank_ef_compress": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p], i32),
+        "cfz_lowrank_ef_decompress": ([i64, i64, i64, i32, p, p, p, p, p, p], i32),
         "cfz_stream_copy": ([p, p, sz, p], i32),
         "cfz_status_string": ([i32], C.c_char_p),
         "cfz_last_error": ([], C.c_char_p),
@@ -219,6 +223,30 @@ def cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, workspace, ws_bytes=None, st
                             _ptr(RU), _ptr(workspace), ws_bytes, _stream(stream)), "cfz_lowrank")
 
 
+def cfz_lowrank_ef_workspace_bytes(batch, m, n, r) -> int:
+    return _lib.cfz_lowrank_ef_workspace_bytes(batch, m, n, r)
+
+
+def cfz_lowrank_ef_warmup(count, x0=None, prev=None, err=None, base=None, stream=None) -> None:
+    _check(_lib.cfz_lowrank_ef_warmup(count, _bf16_ptr(x0), _bf16_ptr(prev), _ptr(err), _ptr(base),
+                                      _stream(stream)), "cfz_lowrank_ef_warmup")
+
+
+def cfz_lowrank_ef_compress(batch, m, n, r, T, x, prev, err, Q0, U, V, RU, workspace,
+                            ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cfz_lowrank_ef_compress(batch, m, n, r, T, _bf16_ptr(x), _bf16_ptr(prev), _ptr(err),
+                                        _ptr(Q0), _ptr(U), _ptr(V), _ptr(RU), _ptr(workspace),
+                                        ws_bytes, _stream(stream)), "cfz_lowrank_ef_compress")
+
+
+def cfz_lowrank_ef_decompress(batch, m, n, r, U, V, RU, base, xhat=None, stream=None) -> None:
+    _check(_lib.cfz_lowrank_ef_decompress(batch, m, n, r, _ptr(U), _ptr(V), _ptr(RU), _ptr(base),
+                                          _bf16_ptr(xhat), _stream(stream)),
+           "cfz_lowrank_ef_decompress")
+
+
 def cfz_stream_copy(src, dst, nbytes=None, stream=None) -> None:
     if nbytes is None:
         nbytes = src.numel() * src.element_size()
@@ -291,3 +319,43 @@ class Receiver:
             self.close()
         except Exception:
             pass
+
+
+class LowrankSender:
+    """Sender of the rank-r compressor inside error feedback, for ``batch`` tensors of m x n:
+    prev (bf16), err (fp32), the workspace and the payload (U, V, RU) in torch tensors."""
+
+    def __init__(self, batch, m, n, r, x0=None, device="cuda", stream=None):
+        self.batch, self.m, self.n, self.r = batch, m, n, r
+        count = batch * m * n
+        self.prev = torch.empty(count, dtype=torch.bfloat16, device=device)
+        self.err = torch.empty(count, dtype=torch.float32, device=device)
+        self.ws = torch.empty(max(cfz_lowrank_ef_workspace_bytes(batch, m, n, r), 1),
+                              dtype=torch.uint8, device=device)
+        self.U = torch.empty((batch, m, r), dtype=torch.float32, device=device)
+        self.V = torch.empty((batch, n, r), dtype=torch.float32, device=device)
+        self.RU = torch.empty((batch, r, r), dtype=torch.float32, device=device)
+        cfz_lowrank_ef_warmup(count, x0, self.prev, self.err, None, stream)
+
+    def residual_bf16(self):
+        """The bf16 residual A of the last step, left at the start of the workspace."""
+        return self.ws[: self.batch * self.m * self.n * 2].view(torch.bfloat16)
+
+    def compress(self, x, Q0, T, stream=None):
+        cfz_lowrank_ef_compress(self.batch, self.m, self.n, self.r, T, x, self.prev, self.err, Q0,
+                                self.U, self.V, self.RU, self.ws, stream=stream)
+        return self.U, self.V, self.RU
+
+
+class LowrankReceiver:
+    """Receiver of the rank-r compressor inside error feedback: the fp32 base."""
+
+    def __init__(self, batch, m, n, r, x0=None, device="cuda", stream=None):
+        self.batch, self.m, self.n, self.r = batch, m, n, r
+        self.base = torch.empty(batch * m * n, dtype=torch.float32, device=device)
+        cfz_lowrank_ef_warmup(batch * m * n, x0, None, None, self.base, stream)
+
+    def decompress(self, U, V, RU, xhat=None, stream=None):
+        cfz_lowrank_ef_decompress(self.batch, self.m, self.n, self.r, U, V, RU, self.base, xhat,
+                                  stream)
+        return xhat

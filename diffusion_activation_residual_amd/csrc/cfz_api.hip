@@ -381,23 +381,53 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
     return cfz::lowrank_workspace_bytes(batch, m, n, r);
 }
 
-cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
-                       const uint16_t *A, const float *Q0, float *U, float *V, float *RU,
-                       void *ws, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shape rules shared by the low-rank entry points (T < 0 is checked where T is taken).
+cfz_status check_lowrank_shape(int64_t batch, int64_t m, int64_t n, int32_t r)
 {
     if (batch < 0 || m <= 0 || n <= 0)
         return fail(CFZ_ERR_SHAPE, "batch = %lld, m = %lld, n = %lld", (long long)batch,
                     (long long)m, (long long)n);
     if (r < 1 || r > 32 || r > m || r > n)
         return fail(CFZ_ERR_SHAPE, "rank r = %d must be in [1, min(32, m, n)]", r);
-    if (T < 0)
-        return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
     if (n % 8 != 0)
         return fail(CFZ_ERR_SHAPE, "n = %lld must be a multiple of 8 (16-byte rows)", (long long)n);
     if (m * n > ((int64_t)1 << 30))
         return fail(CFZ_ERR_SHAPE, "m * n = %lld exceeds 2^30 elements per matrix", (long long)(m * n));
     if (m > (1 << 20) || n > (1 << 20) || batch > (1 << 20))
         return fail(CFZ_ERR_SHAPE, "sizes too large");
+    return CFZ_OK;
+}
+
+cfz_status check_lowrank_ef_shape(int64_t batch, int64_t m, int64_t n, int32_t r)
+{
+    cfz_status st = check_lowrank_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (cfz::lowrank_ef_update_blocks(batch, m, n) >= ((int64_t)1 << 31) ||
+        batch * m * n / 4 / 256 >= ((int64_t)1 << 31))
+        return fail(CFZ_ERR_SHAPE, "batch * m * n too large for one launch");
+    return CFZ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                       const uint16_t *A, const float *Q0, float *U, float *V, float *RU,
+                       void *ws, size_t ws_bytes, void *stream)
+{
+    cfz_status st = check_lowrank_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (T < 0)
+        return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
     if (batch == 0)
         return CFZ_OK;
     if (!A || !Q0 || !U || !V || !RU)
@@ -414,6 +444,89 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
     hipError_t e = cfz::launch_lowrank(a, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "low-rank launch");
+    return CFZ_OK;
+}
+
+size_t cfz_lowrank_ef_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r)
+{
+    if (batch < 0 || m <= 0 || n <= 0 || r < 1 || r > 32 || r > m || r > n || n % 8 != 0 ||
+        m > (1 << 20) || n > (1 << 20) || batch > (1 << 20) || m * n > ((int64_t)1 << 30))
+        return 0;
+    return align256((size_t)(batch * m * n) * 2) + cfz::lowrank_workspace_bytes(batch, m, n, r);
+}
+
+cfz_status cfz_lowrank_ef_warmup(int64_t count, const uint16_t *x0, uint16_t *prev, float *err,
+                                 float *base, void *stream)
+{
+    if (count < 0 || count % 8 != 0)
+        return fail(CFZ_ERR_SHAPE, "count = %lld must be a non-negative multiple of 8",
+                    (long long)count);
+    if (!aligned16(x0) || !aligned16(prev) || !aligned16(err) || !aligned16(base))
+        return fail(CFZ_ERR_ALIGN, "buffers must be 16-byte aligned");
+    if (count == 0 || (!prev && !err && !base))
+        return CFZ_OK;
+    hipError_t e = cfz::launch_warmup(x0, prev, base, err, false, count / 8, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "warm-up launch");
+    return CFZ_OK;
+}
+
+cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                                   const uint16_t *x, uint16_t *prev, float *err, const float *Q0,
+                                   float *U, float *V, float *RU, void *ws, size_t ws_bytes,
+                                   void *stream)
+{
+    cfz_status st = check_lowrank_ef_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (T < 0)
+        return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
+    if (batch == 0)
+        return CFZ_OK;
+    if (!x || !prev || !err || !Q0 || !U || !V || !RU)
+        return fail(CFZ_ERR_NULL, "x, prev, err, Q0, U, V and RU are required");
+    if (!aligned16(x) || !aligned16(prev) || !aligned16(err) || !aligned16(Q0) || !aligned16(U) ||
+        !aligned16(V) || !aligned16(RU))
+        return fail(CFZ_ERR_ALIGN, "every buffer must be 16-byte aligned");
+    const size_t a_bytes = align256((size_t)(batch * m * n) * 2);
+    const size_t need = a_bytes + cfz::lowrank_workspace_bytes(batch, m, n, r);
+    if (!ws || ws_bytes < need)
+        return fail(CFZ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (((uintptr_t)ws & 255u) != 0)
+        return fail(CFZ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    hipStream_t hs = (hipStream_t)stream;
+    uint16_t *A = (uint16_t *)ws;
+    hipError_t e = cfz::launch_lowrank_ef_residual(x, prev, err, A, batch * m * n, hs);
+    if (e != hipSuccess)
+        return hip_fail(e, "residual launch");
+    cfz::LowrankArgs a{batch, m, n, r, T, A, Q0, U, V, RU, (uint8_t *)ws + a_bytes};
+    e = cfz::launch_lowrank(a, hs);
+    if (e != hipSuccess)
+        return hip_fail(e, "low-rank launch");
+    e = cfz::launch_lowrank_ef_update(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, hs);
+    if (e != hipSuccess)
+        return hip_fail(e, "update launch");
+    return CFZ_OK;
+}
+
+cfz_status cfz_lowrank_ef_decompress(int64_t batch, int64_t m, int64_t n, int32_t r,
+                                     const float *U, const float *V, const float *RU, float *base,
+                                     uint16_t *xhat, void *stream)
+{
+    cfz_status st = check_lowrank_ef_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (batch == 0)
+        return CFZ_OK;
+    if (!U || !V || !RU || !base)
+        return fail(CFZ_ERR_NULL, "U, V, RU and base are required");
+    if (!aligned16(U) || !aligned16(V) || !aligned16(RU) || !aligned16(base) || !aligned16(xhat))
+        return fail(CFZ_ERR_ALIGN, "every buffer must be 16-byte aligned");
+    hipError_t e = cfz::launch_lowrank_ef_update(batch, m, n, r, U, V, RU, 1.0f, base, xhat,
+                                                 (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "update launch");
     return CFZ_OK;
 }
 

@@ -49,4 +49,12 @@ struct LowrankArgs {
 size_t lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int r);
 hipError_t launch_lowrank(const LowrankArgs &a, hipStream_t st);
 
+// rank-r compressor inside the error-feedback loop
+hipError_t launch_lowrank_ef_residual(const uint16_t *x, uint16_t *prev, float *err, uint16_t *A,
+                                      int64_t count, hipStream_t st);
+hipError_t launch_lowrank_ef_update(int64_t batch, int64_t m, int64_t n, int r, const float *U,
+                                    const float *V, const float *RU, float sign, float *Y,
+                                    uint16_t *xhat, hipStream_t st);
+int64_t lowrank_ef_update_blocks(int64_t batch, int64_t m, int64_t n);
+
 }  // namespace cfz

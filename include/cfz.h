@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CFZ_ABI_VERSION 2
+#define CFZ_ABI_VERSION 3
 
 typedef enum {
     CFZ_OK = 0,
@@ -189,6 +189,54 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
 cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
                        const uint16_t *A_bf16, const float *Q0, float *U, float *V, float *RU,
                        void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* ---- The rank-r compressor inside the error-feedback loop ----------------
+ * The pages send step-wise residuals with error feedback (abstract) and give
+ * the subspace iteration as a compressor (Algorithm 3).  Combined like the
+ * DELTA mode of the quantizer, on `batch` independent m x n tensors:
+ *   sender:   r = (x - prev) + err (fp32);  A = bf16(r), round to nearest even;
+ *             (U, R_U, V) = Algorithm 3 on A;  err' = r - (U R_U) V^T;  prev' = x
+ *   receiver: base' = base + (U R_U) V^T;  xhat = bf16(base')
+ * The payload is (U, R_U, V) in fp32.  Sender and receiver form (U R_U) V^T
+ * with the same kernel (fp32, v_mfma_f32_16x16x4_f32), so with the same
+ * factors their reconstructions agree bit for bit.
+ * Layouts: x, prev, xhat bf16 and err, base fp32, all [batch][m][n]; U, V, RU
+ * as for cfz_lowrank.  Sizes as for cfz_lowrank, plus batch * ceil(m / 64) *
+ * ceil(n / 128) < 2^31.  Every pointer 16-byte aligned; the caller owns all
+ * memory.  Calls are asynchronous on hip_stream; tensors of one state must not
+ * be used on two streams at once. */
+
+/* Workspace for cfz_lowrank_ef_compress in bytes (0 if the sizes are
+ * invalid): A, the bf16 residual [batch][m][n], at offset 0 -- left there by
+ * the call, for inspection -- then, from the next 256-byte boundary, the
+ * workspace of cfz_lowrank. */
+size_t cfz_lowrank_ef_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r);
+
+/* Warm-up (t = 0, the uncompressed step; reproducibility table, "Dataset
+ * Splits"): prev = x0 and err = 0 at the sender, base = fp32(x0) at the
+ * receiver, over `count` elements (a multiple of 8).  prev, err and base may
+ * each be NULL (not written); x0 NULL means zeros.
+ * Errors: CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_HIP. */
+cfz_status cfz_lowrank_ef_warmup(int64_t count, const uint16_t *x0_bf16, uint16_t *prev_bf16,
+                                 float *err, float *base, void *hip_stream);
+
+/* One sender step (above).  Q0: [batch][n][r] fp32 random sample of the
+ * subspace iteration; passing the previous step's V warm-starts it.  Outputs
+ * U, V, RU; updates prev and err in place.  Workspace: at least
+ * cfz_lowrank_ef_workspace_bytes(batch, m, n, r) bytes, 256-byte aligned.
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_WORKSPACE,
+ * CFZ_ERR_HIP; on error nothing is enqueued. */
+cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                                   const uint16_t *x_bf16, uint16_t *prev_bf16, float *err,
+                                   const float *Q0, float *U, float *V, float *RU,
+                                   void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* One receiver step (above): base += (U R_U) V^T; xhat_bf16 (nullable)
+ * receives bf16(base') rounded to nearest even.
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_HIP. */
+cfz_status cfz_lowrank_ef_decompress(int64_t batch, int64_t m, int64_t n, int32_t r,
+                                     const float *U, const float *V, const float *RU, float *base,
+                                     uint16_t *xhat_bf16, void *hip_stream);
 
 /* Measurement aid: a plain streaming copy of `bytes` bytes (multiple of 16,
  * both pointers 16-byte aligned) on hip_stream, used to calibrate HBM

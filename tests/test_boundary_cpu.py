@@ -14,10 +14,10 @@ MISALIGNED = 0x10008
 
 def test_library_exports_every_declared_function():
     names = cfz.header_functions()
-    assert len(names) == 16
+    assert len(names) == 20
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
-    assert cfz.cfz_abi_version() == 2
+    assert cfz.cfz_abi_version() == 3
 
 
 def test_status_strings():
@@ -133,6 +133,43 @@ def test_lowrank_validation():
     assert call(ws_bytes=ws_need - 1) == cfz.CFZ_ERR_WORKSPACE
     assert call(ws=ALIGNED + 16) == cfz.CFZ_ERR_ALIGN
     assert call(batch=0, A=None) == cfz.CFZ_OK  # empty batch: no-op
+
+
+def test_lowrank_ef_validation():
+    lib = cfz._lib
+    b, m, n, r = 2, 128, 192, 8
+    need = cfz.cfz_lowrank_ef_workspace_bytes(b, m, n, r)
+    a_bytes = (b * m * n * 2 + 255) // 256 * 256
+    assert need == a_bytes + cfz.cfz_lowrank_workspace_bytes(b, m, n, r)
+    assert cfz.cfz_lowrank_ef_workspace_bytes(b, m, 190, r) == 0
+    assert cfz.cfz_lowrank_ef_workspace_bytes(b, m, n, 33) == 0
+
+    def comp(batch=b, mm=m, nn=n, rr=r, T=1, x=ALIGNED, prev=ALIGNED, err=ALIGNED, Q0=ALIGNED,
+             U=ALIGNED, V=ALIGNED, RU=ALIGNED, ws=ALIGNED, ws_bytes=need):
+        return lib.cfz_lowrank_ef_compress(batch, mm, nn, rr, T, x, prev, err, Q0, U, V, RU, ws,
+                                           ws_bytes, None)
+
+    assert comp(rr=0) == cfz.CFZ_ERR_SHAPE
+    assert comp(nn=196) == cfz.CFZ_ERR_SHAPE
+    assert comp(T=-1) == cfz.CFZ_ERR_SHAPE
+    assert comp(x=None) == cfz.CFZ_ERR_NULL
+    assert comp(err=None) == cfz.CFZ_ERR_NULL
+    assert comp(prev=MISALIGNED) == cfz.CFZ_ERR_ALIGN
+    assert comp(ws_bytes=need - 1) == cfz.CFZ_ERR_WORKSPACE
+    assert comp(ws=ALIGNED + 16) == cfz.CFZ_ERR_ALIGN
+    assert comp(batch=0, x=None) == cfz.CFZ_OK
+
+    def dec(batch=b, U=ALIGNED, V=ALIGNED, RU=ALIGNED, base=ALIGNED, xhat=None, rr=r):
+        return lib.cfz_lowrank_ef_decompress(batch, m, n, rr, U, V, RU, base, xhat, None)
+
+    assert dec(base=None) == cfz.CFZ_ERR_NULL
+    assert dec(xhat=MISALIGNED) == cfz.CFZ_ERR_ALIGN
+    assert dec(rr=40) == cfz.CFZ_ERR_SHAPE
+    assert dec(batch=0, base=None) == cfz.CFZ_OK
+    assert lib.cfz_lowrank_ef_warmup(12, None, ALIGNED, None, None, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_lowrank_ef_warmup(16, MISALIGNED, ALIGNED, None, None, None) == \
+        cfz.CFZ_ERR_ALIGN
+    assert lib.cfz_lowrank_ef_warmup(0, None, ALIGNED, ALIGNED, ALIGNED, None) == cfz.CFZ_OK
 
 
 def test_stream_copy_validation():
