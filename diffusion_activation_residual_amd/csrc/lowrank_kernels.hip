@@ -113,9 +113,12 @@ constexpr int kAqTiles = 2;                     // 16-row MFMA tiles per wave
 constexpr int kAqRows = 4 * 16 * kAqTiles;      // rows of A per work-group
 
 // One work-group: kAqRows rows of A against all of Q, 64 columns of A per step.
-// Pipeline: A tiles two steps ahead in two statically named register stages
-// (the loop is unrolled by two so no register is copied), Q tiles one step
-// ahead in registers and double-buffered in LDS, one barrier per step.
+// A is loaded 8 rows x 128 bytes per wave instruction (whole cache lines) and
+// passed through a wave-private LDS tile into MFMA operand layout (16 rows x 8
+// columns per lane group), which read straight from memory would split every
+// instruction into 16 half lines.  Pipeline: A tiles kPipe steps ahead in
+// statically named register stages, Q tiles one step ahead in registers and
+// double-buffered in LDS, one work-group barrier per step.
 // OUT_OPS: write Y in operand layout (hi/lo planes, rows up to mp, zero beyond
 // m); otherwise write Y as fp32 [m][r].
 template <int RP, bool OUT_OPS>
@@ -130,6 +133,7 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
     const bf16x8 *qlo = qhi + (np / 8) * RP;
 
     __shared__ bf16x8 sq[2][2][8][RP];  // [buffer][hi, lo][k block][column]
+    __shared__ bf16x8 sa[4][16 * kAqTiles][9];  // [wave][row][8 column chunks + pad]
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
     const int64_t row0 = (int64_t)blk * kAqRows;
     const int64_t rows_here = (m - row0 < kAqRows) ? m - row0 : kAqRows;
@@ -140,15 +144,14 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
     constexpr int QPT = (QE + kThreads - 1) / kThreads;
     const int64_t last_tile = np - 64;             // Q loads past the end re-read a valid tile
 
-    auto a_off = [&](int t, int64_t col) -> uint32_t {
-        const int64_t rr = wave * 16 * kAqTiles + t * 16 + li;
-        return (rr < rows_here && col < n) ? (uint32_t)((rr * n + col) * 2) : kOOB;
-    };
+    // load instruction p: rows 8 p + lane / 8 of the wave's rows, column chunk lane % 8
     auto load_a = [&](int64_t k0, bf16x8 (&av)[kAqTiles][2]) {
 #pragma unroll
-        for (int t = 0; t < kAqTiles; ++t) {
-            av[t][0] = buf_load16(ra, a_off(t, k0 + 8 * g));
-            av[t][1] = buf_load16(ra, a_off(t, k0 + 32 + 8 * g));
+        for (int p = 0; p < 2 * kAqTiles; ++p) {
+            const int64_t rr = wave * 16 * kAqTiles + 8 * p + (lane >> 3);
+            const int64_t col = k0 + 8 * (lane & 7);
+            av[p / 2][p % 2] = buf_load16(
+                ra, (rr < rows_here && col < n) ? (uint32_t)((rr * n + col) * 2) : kOOB);
         }
     };
     auto load_q = [&](int64_t k0, bf16x8 (&qv)[QPT]) {
@@ -177,7 +180,23 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
         for (int j = 0; j < RP / 16; ++j)
             acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, const bf16x8 (&av)[kAqTiles][2]) {
+    auto compute = [&](int buf, const bf16x8 (&ld)[kAqTiles][2]) {
+        // the loaded rows into the wave's tile, then the operands out of it
+#pragma unroll
+        for (int p = 0; p < 2 * kAqTiles; ++p)
+            sa[wave][8 * p + (lane >> 3)][lane & 7] = ld[p / 2][p % 2];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bf16x8 av[kAqTiles][2];
+#pragma unroll
+        for (int t = 0; t < kAqTiles; ++t) {
+            av[t][0] = sa[wave][16 * t + li][g];
+            av[t][1] = sa[wave][16 * t + li][4 + g];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int t = 0; t < kAqTiles; ++t)
 #pragma unroll
