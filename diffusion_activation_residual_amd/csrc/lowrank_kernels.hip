@@ -727,6 +727,38 @@ lr_apply_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_
     }
 }
 
+// ------------------------------------------------------------------ operand layout
+
+// M (fp32 [L][r]) into the operand layout of A Q: one thread per slot (8 rows of
+// one column), split into bf16 hi and lo planes; rows L..Lp-1 and columns r..RP-1
+// are zeros.
+template <int RP>
+__global__ void __launch_bounds__(kThreads)
+lr_ops_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_t Lp, int r,
+              uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_ops, int64_t slots_per_mat,
+              int64_t batch)
+{
+    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t b = id / slots_per_mat, slot = id % slots_per_mat;
+    if (b >= batch)
+        return;
+    const int64_t kb = slot / RP;
+    const int c = (int)(slot % RP);
+    const float *Mb = M + b * m_stride;
+    bf16x8 *hi = (bf16x8 *)(ws + (size_t)b * layer_bytes + off_ops);
+    bf16x8 *lo = hi + (Lp / 8) * RP;
+    bf16x8 h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = 8 * kb + i;
+        const float q = (row < L && c < r) ? Mb[row * r + c] : 0.0f;
+        h[i] = (__bf16)q;
+        l[i] = (__bf16)(q - (float)h[i]);
+    }
+    hi[slot] = h;
+    lo[slot] = l;
+}
+
 // ------------------------------------------------------------------ host orchestration
 
 template <int RP>
@@ -765,10 +797,22 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
     const int aq_blocks = (int)(Ly.mp / kAqRows);
     const int aty_blocks = (int)((a.n + kAtyCols - 1) / kAtyCols);
 
-    // step 1: orthonormalise the random sample
-    if ((e = run_orth<RP>(Ly, a.batch, a.Q0, a.n * a.r, a.n, a.r, ws, a.V, a.n * a.r, true,
-                          nullptr, st)) != hipSuccess)
-        return e;
+    // step 1: orthonormalise the random sample.  With T >= 1 the sample only enters
+    // through qf(A^T A Q0) = qf(A^T A orth(Q0)) (Q0 = orth(Q0) R0 with R0 upper
+    // triangular, positive diagonal), so Q0 goes into the first product as it is; only
+    // T = 0 returns orth(Q0) itself as V.
+    if (a.T == 0) {
+        if ((e = run_orth<RP>(Ly, a.batch, a.Q0, a.n * a.r, a.n, a.r, ws, a.V, a.n * a.r, true,
+                              nullptr, st)) != hipSuccess)
+            return e;
+    } else {
+        const int64_t slots = (Ly.np / 8) * RP, total = slots * a.batch;
+        hipLaunchKernelGGL((lr_ops_kernel<RP>), dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, a.Q0, a.n * a.r, a.n, Ly.np, a.r, ws,
+                           Ly.layer_bytes, Ly.off_qops, slots, a.batch);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
     for (int t = 0; t < a.T; ++t) {
         hipLaunchKernelGGL((lr_aq_kernel<RP, true>), dim3((unsigned)(aq_blocks * a.batch)),
                            dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
