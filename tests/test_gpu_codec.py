@@ -426,3 +426,45 @@ def test_grouped_launch_matches_oracle(bits, group, mode, sb):
             _compare_step(f"group t{t} entry {i}", snd[i], rcv[i], snd[i].codes, snd[i].scales,
                           osnd[i], orcv[i], oc, osc, xh[i], ox)
     assert all(cfz.cfz_state_steps(s.handle) == 3 for s in snd)
+
+
+def test_lost_payload_then_rewarm_in_place():
+    """OFF mode on the GPU: a skipped decode makes the sender's and receiver's bases differ;
+    re-warming both states in place (cfz_state_create on the same buffers with an
+    uncompressed activation) gives the bits of a fresh run from there, step by step, and the
+    oracle's."""
+    rows, cols = 128, 512
+    xs = [x[0] for x in _ar1(rows, cols, 9, seed=31)]
+    say("[gpu] lost payload and re-warm")
+    gs = cfz.Sender(rows, cols, 4, 64, cfz.CFZ_EF_OFF, x0=xs[0].to(DEV))
+    gr = cfz.Receiver(rows, cols, 4, 64, x0=xs[0].to(DEV))
+    for t in range(1, 5):
+        codes, scales = gs.compress(xs[t].to(DEV))
+        if t != 2:
+            gr.decompress(codes, scales)
+        torch.cuda.synchronize()
+        assert torch.equal(sbits_t(gs.base), sbits_t(gr.base)) == (t < 2), f"step {t}"
+    # in place: new handles on the same buffers, warmed from x_4
+    x4 = xs[4].to(DEV)
+    cfz.cfz_state_destroy(gs.handle)
+    cfz.cfz_state_destroy(gr.handle)
+    gs.handle = cfz.cfz_state_create(gs.desc, None, gs.base, None, x4)
+    gr.handle = cfz.cfz_state_create(gr.desc, None, gr.base, None, x4)
+    fs = cfz.Sender(rows, cols, 4, 64, cfz.CFZ_EF_OFF, x0=x4)
+    fr = cfz.Receiver(rows, cols, 4, 64, x0=x4)
+    n = rows * cols
+    os_ = oracle.Sender(n, 4, 64, oracle.OFF, x0=u16(xs[4]))
+    or_ = oracle.Receiver(n, 4, 64, x0=u16(xs[4]))
+    for t in range(5, 9):
+        c1, s1 = gs.compress(xs[t].to(DEV))
+        gr.decompress(c1, s1)
+        c2, s2 = fs.compress(xs[t].to(DEV))
+        fr.decompress(c2, s2)
+        oc, osc = os_.compress(u16(xs[t]))
+        or_.decompress(oc, osc)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2) and torch.equal(sbits_t(gr.base), sbits_t(fr.base))
+        assert torch.equal(sbits_t(gs.base), sbits_t(gr.base))
+        _compare_step(f"re-warmed step {t}", gs, gr, c1, s1, os_, or_, oc, osc)
+    for h in (gs, gr, fs, fr):
+        h.close()

@@ -481,3 +481,62 @@ def test_bf16_state_step_is_fp32_step_rounded(mode, bits, group):
     r32.decompress(c32, sc32)
     r16.decompress(c32, sc32)
     assert np.array_equal(_rne_bf16_numpy(r32.base), r16.base)
+
+
+# ---------------------------------------------------------------- lost payload and recovery
+
+def _stream_xs(steps, seed=21):
+    sp = SPECS["flux"]
+    st = AR1Stream(1, 128, 512, sp.alpha, sp.noise, 0.01, seed=seed, key="flux")
+    return [bf16_np(st.next()) for _ in range(steps)]
+
+
+def test_lost_payload_is_detected_and_rewarm_recovers():
+    """Closed loop (OFF): the sender's and receiver's bases are bit-identical after every
+    step, so one skipped decode shows up as a mismatch and stays.  Re-warming both sides from
+    an uncompressed activation (the warm-up step) gives exactly the states of a fresh run
+    started there."""
+    xs = _stream_xs(10)
+    n = xs[0].size
+    snd = oracle.Sender(n, 4, 64, oracle.OFF, x0=xs[0])
+    rcv = oracle.Receiver(n, 4, 64, x0=xs[0])
+    for t in range(1, 6):
+        codes, scales = snd.compress(xs[t])
+        if t != 3:  # the payload of step 3 is lost
+            rcv.decompress(codes, scales)
+        assert np.array_equal(snd.base, rcv.base) == (t < 3), f"step {t}"
+    # re-warm both from x_5, next to a fresh pair started at x_5
+    snd = oracle.Sender(n, 4, 64, oracle.OFF, x0=xs[5])
+    rcv = oracle.Receiver(n, 4, 64, x0=xs[5])
+    fs = oracle.Sender(n, 4, 64, oracle.OFF, x0=xs[5])
+    fr = oracle.Receiver(n, 4, 64, x0=xs[5])
+    for t in range(6, 10):
+        c1, s1 = snd.compress(xs[t])
+        c2, s2 = fs.compress(xs[t])
+        rcv.decompress(c1, s1)
+        fr.decompress(c2, s2)
+        assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+        assert np.array_equal(snd.base, rcv.base) and np.array_equal(rcv.base, fr.base)
+
+
+def test_lost_payload_in_delta_mode_shows_in_the_error():
+    """DELTA: the receiver tracks X - E, so its error stays at the quantizer's level; a lost
+    payload leaves it behind by that step's whole residual, which never comes back."""
+    xs = _stream_xs(10, seed=22)
+    n = xs[0].size
+
+    def errs(skip):
+        snd = oracle.Sender(n, 4, 64, oracle.DELTA, x0=xs[0])
+        rcv = oracle.Receiver(n, 4, 64, x0=xs[0])
+        out = []
+        for t in range(1, 10):
+            codes, scales = snd.compress(xs[t])
+            if t != skip:
+                rcv.decompress(codes, scales)
+            xt = bf16_bits_to_f64(xs[t])
+            out.append(np.linalg.norm(xt - rcv.base) / np.linalg.norm(xt))
+        return out
+
+    clean, lost = errs(None), errs(4)
+    assert lost[:3] == clean[:3]
+    assert all(l > 3 * c for l, c in zip(lost[3:], clean[3:]))
