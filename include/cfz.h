@@ -51,8 +51,8 @@ typedef enum {
 
 /* How the sender forms the residual and carries the compression error.
  *   DELTA   (default): r = (x - prev) + err; prev' = x; err' = r - q s.
- *           Error feedback on step-wise activation differences: the receiver's
- *           base then equals x - err' after every step.
+ *           Error feedback on the change between consecutive steps: the
+ *           receiver's base then equals x - err' after every step.
  *   LITERAL: r = (x - base) + err; err' = r - q s; base' = base + q s.
  *           The carried error is added on top of a base that already absorbs
  *           it; kept to reproduce that reading, which is unstable at 2 bits.

@@ -10,14 +10,15 @@
  *
  * Sources (paper: "Accelerating Parallel Diffusion Model Serving with
  * Residual Compression", Luo et al., NeurIPS 2025):
- *   - abstract: only compressed residuals (step-wise activation differences)
- *     are transmitted, with lightweight error feedback against accumulation;
+ *   - abstract: what travels between devices is the compressed change of an
+ *     activation from one denoising step to the next, and an error-feedback
+ *     term keeps the compression error from building up;
  *   - reproducibility table, "Dataset Splits": at least one uncompressed
  *     warm-up step initialises the base tensor used for later residuals;
  *   - reproducibility table, "Pseudocode", Algorithm 3 (Subspace Iteration):
  *     random orthonormal Q; T times Z = A^T A Q, Q = orth(Z); U = orth(AQ); V = Q.
- *   - xDiT issue #573 (proposal to integrate CompactFusion): residuals plus
- *     error feedback cut communication 8-16x.
+ *   - xDiT issue #573 (proposal to integrate CompactFusion): the residual
+ *     scheme with error feedback reduces communication by a factor of 8 to 16.
  *
  * Readings taken where the pages are silent (each one is also listed with the
  * design notes of the library):
