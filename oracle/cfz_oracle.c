@@ -464,7 +464,7 @@ void oracle_lowrank_ef_compress(int64_t m, int64_t n, int r, int T, const uint16
                                 uint16_t *prev, float *err, const float *Q0, uint16_t *A,
                                 double *U, double *V, double *RU)
 {
-    uint16_t *a = A ? A : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(m * n));
+    uint16_t *a = A ? A : (uint16_t *)calloc((size_t)(m * n), sizeof(uint16_t));
     for (int64_t j = 0; j < m * n; ++j) {
         float rj = (bf16_to_float(x[j]) - bf16_to_float(prev[j])) + err[j];
         err[j] = rj;
