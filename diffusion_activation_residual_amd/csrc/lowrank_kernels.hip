@@ -275,18 +275,28 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
 
 constexpr int kAtyCols = 64;  // columns of A per work-group (4 waves x 16)
 
-// LDS row of slab column c.  The 8 loader lanes that hold the same rows of 8
-// different column chunks write columns 8 t + s (t = 0..7); mapping them to rows
-// with distinct low bits puts them in distinct bank groups, and the 8 columns a
-// reader lane group takes (16 consecutive) stay distinct as well.
-__device__ __forceinline__ int slab_col(int c) { return c ^ ((c >> 3) & 7); }
 constexpr int kAtyRows = 64;  // rows of A per pipeline step (two 32-row MFMA k steps)
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element
+// j % 4 of the 4-element chunks addressed by lanes j / 4, 4 + j / 4, 8 + j / 4
+// and 12 + j / 4 (measured on gfx950).  So if lane i of a group addresses row
+// base + i / 4, columns c0 + 4 (i % 4) .. + 3 of a row-major slab, lane j gets
+// rows base .. base + 3 of column c0 + j: half an MFMA operand.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p));
+}
+
 // One work-group: 64 columns of A (wave w owns columns 16w..16w+15) against all
-// rows.  Each 64-row slab of A is loaded with coalesced 16-byte loads and stored
-// transposed in LDS, so that a lane's MFMA operand (8 consecutive rows of one
-// column) is one 16-byte LDS read.  Same pipeline as A Q: slabs two steps ahead
-// in static register stages, Y tiles one step ahead, double-buffered LDS.
+// rows.  Each 64-row slab of A is loaded with coalesced 16-byte loads, stored in
+// LDS as it is (one 16-byte store per load) and read back with the transposing
+// LDS load, so that a lane's MFMA operand (8 consecutive rows of one column) is
+// two 8-byte reads.  Same pipeline as A Q: slabs kPipe steps ahead in static
+// register stages, Y tiles one step ahead, double-buffered LDS.
 template <int RP>
 __global__ void __launch_bounds__(kThreads)
 lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
@@ -299,8 +309,8 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     const bf16x8 *ylo = yhi + (mp / 8) * RP;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)b * m * n, (uint32_t)(m * n * 2));
 
-    constexpr int SROW = kAtyRows + 8;             // padded row of the transposed slab (144 B)
-    __shared__ __attribute__((aligned(16))) uint16_t sa[2][kAtyCols][SROW];
+    constexpr int SCOL = kAtyCols + 8;             // padded slab row: 144 B, rows 4 banks apart
+    __shared__ __attribute__((aligned(16))) uint16_t sa[2][kAtyRows][SCOL];
     __shared__ bf16x8 sy[2][2][kAtyRows / 8][RP];  // [buffer][hi, lo][k block][column]
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
@@ -333,12 +343,7 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     auto store = [&](int buf, const u32x4 (&av)[2], const bf16x8 (&yv)[YPT]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const uint32_t w = av[h][s >> 1];
-                sa[buf][slab_col(8 * tcc + s)][trow + 32 * h] =
-                    (uint16_t)((s & 1) ? (w >> 16) : (w & 0xffffu));
-            }
+            *(u32x4 *)&sa[buf][trow + 32 * h][8 * tcc] = av[h];
 #pragma unroll
         for (int p = 0; p < YPT; ++p) {
             const int e = threadIdx.x + p * kThreads;
@@ -354,7 +359,11 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < kAtyRows / 32; ++ks) {
-            const bf16x8 aop = *(const bf16x8 *)&sa[buf][slab_col(wave * 16 + li)][32 * ks + 8 * g];
+            // rows 32 ks + 8 g .. + 7 of column 16 wave + li
+            const uint16_t *p = &sa[buf][32 * ks + 8 * g + (li >> 2)][wave * 16 + 4 * (li & 3)];
+            const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * SCOL);
+            const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const bf16x8 aop = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
             for (int jt = 0; jt < RP / 16; ++jt) {
                 acc[jt] = mfma(aop, sy[buf][0][4 * ks + g][jt * 16 + li], acc[jt]);
