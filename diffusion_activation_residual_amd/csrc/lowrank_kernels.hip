@@ -136,7 +136,9 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
     __shared__ bf16x8 sa[4][16 * kAqTiles][9];  // [wave][row][8 column chunks + pad]
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
     const int64_t row0 = (int64_t)blk * kAqRows;
-    const int64_t rows_here = (m - row0 < kAqRows) ? m - row0 : kAqRows;
+    // rows of A this work-group owns; 0 for a block wholly in the padding past m (its
+    // loads then all return zeros: a negative count would make the buffer size wrap)
+    const int64_t rows_here = m - row0 <= 0 ? 0 : (m - row0 < kAqRows ? m - row0 : kAqRows);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(A + (int64_t)b * m * n + row0 * n, (uint32_t)(rows_here * n * 2));
 
