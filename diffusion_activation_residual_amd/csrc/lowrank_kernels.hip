@@ -111,6 +111,7 @@ __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t
 constexpr int kPipe = 4;                        // register stages of the A-streaming pipelines
 constexpr int kAqTiles = 2;                     // 16-row MFMA tiles per wave
 constexpr int kAqRows = 4 * 16 * kAqTiles;      // rows of A per work-group
+static_assert(128 % kAqRows == 0, "A Q blocks must tile m padded to 128 (Layout::mp)");
 
 // One work-group: kAqRows rows of A against all of Q, 64 columns of A per step.
 // A is loaded 8 rows x 128 bytes per wave instruction (whole cache lines) and
