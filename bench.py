@@ -202,6 +202,90 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
                 "bytes_per_elem": 10}}
 
 
+def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
+    """CogVideoX-2b share at sequence-parallel degree 4: 30 layers x {K, V} of 4388 x 1920
+    bf16 (AR(1), alpha 0.97), DELTA, one grouped compress and one grouped decode launch per
+    layer (its K and V), replayed from HIP graphs."""
+    from synth import SPECS, AR1Stream
+
+    sp = SPECS["cogvideox"]
+    T, rows, cols = sp.tensors, sp.rows, sp.cols
+    n = rows * cols
+    gen = AR1Stream.from_spec(sp, seed=0, device=dev)
+    X = torch.empty((pool + 1, T, n), dtype=torch.bfloat16, device=dev)
+    for s_ in range(pool + 1):
+        X[s_] = gen.next().reshape(T, n)
+    del gen
+    prev = torch.empty((T, n), dtype=torch.bfloat16, device=dev)
+    err = torch.empty((T, n), dtype=torch.float32, device=dev)
+    base = torch.empty((T, n), dtype=torch.float32, device=dev)
+    codes = torch.empty((T, n * bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, n // group), dtype=torch.float32, device=dev)
+    sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER)
+    rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
+    layers = [(2 * l, 2 * l + 1) for l in range(T // 2)]
+
+    def states():
+        return ([cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)],
+                [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)])
+
+    snd, rcv = states()
+
+    def compress_phase(slot):
+        for c in layers:
+            cfz.cfz_compress_group([snd[i] for i in c], [X[slot, i] for i in c],
+                                   [codes[i] for i in c], [scales[i] for i in c])
+
+    def decode_phase():
+        for c in layers:
+            cfz.cfz_decompress_group([rcv[i] for i in c], [codes[i] for i in c],
+                                     [scales[i] for i in c])
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    gc = {}
+    for s_ in range(1, pool + 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            compress_phase(s_)
+        gc[s_] = g
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd, stream=cap):
+        decode_phase()
+    torch.cuda.synchronize()
+    for h in snd + rcv:  # capture only recorded the launches; start from a fresh warm-up
+        cfz.cfz_state_destroy(h)
+    snd[:], rcv[:] = states()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps + 1):  # the first step is an untimed warm-up
+        if k == 1:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        ev[k][0].record()
+        gc[1 + k % pool].replay()
+        ev[k][1].record()
+        gd.replay()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / (steps * len(layers))
+    td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / (steps * len(layers))
+    for h in snd + rcv:
+        cfz.cfz_state_destroy(h)
+    bc, bd = algorithmic_bytes(bits, group)
+    per = 2 * n  # elements per launch
+    return {"workload": f"cogvideox-2b-share {T} tensors of {rows}x{cols}, int{bits} g{group}, "
+                        "delta, one grouped launch per layer (K and V), replayed from HIP graphs",
+            "steps": steps,
+            "activation_GB/s": round(2 * n * T * steps / elapsed / 1e9, 2),
+            "compress": {"avg_launch_us": round(tc * 1e6, 3), "GB/s": round(bc * per / tc / 1e9, 1),
+                         "frac_hbm_peak": round(bc * per / tc / 1e9 / HBM_PEAK_GBS, 4)},
+            "decode": {"avg_launch_us": round(td * 1e6, 3), "GB/s": round(bd * per / td / 1e9, 1),
+                       "frac_hbm_peak": round(bd * per / td / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
 def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
     """The fp64 CPU oracle on one layer per rank; per-call figures scale that by the batch."""
     import numpy as np
@@ -233,6 +317,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--no-batched", action="store_true", help="skip the one-launch-per-step int2 leg")
     ap.add_argument("--no-lowrank", action="store_true", help="skip the subspace-iteration leg")
+    ap.add_argument("--no-cogvideox", action="store_true",
+                    help="skip the CogVideoX-2b-share legs (int4 g64 and int2 g32)")
     ap.add_argument("--launch", choices=("layer", "tensor", "step"), default="layer",
                     help="tensors per launch: K+V of a layer (default), one, or the whole step")
     ap.add_argument("--no-modes", action="store_true", help="skip the other launch granularities")
@@ -476,6 +562,11 @@ def main():
         print("[bench] batched int2 leg", file=sys.stderr, flush=True)
         line["batched_int2_g32"] = bench_batched(cfz, torch, X, slots, T * rows, cols, 2, 32,
                                                  steps=min(K, 10))
+    if not args.no_cogvideox:
+        for cb, cg in ((4, 64), (2, 32)):
+            print(f"[bench] CogVideoX-share leg, int{cb} g{cg}", file=sys.stderr, flush=True)
+            line[f"cogvideox_int{cb}_g{cg}"] = bench_cogvideox(cfz, torch, dev, cb, cg)
+            torch.cuda.empty_cache()
     if not args.no_lowrank:
         print("[bench] subspace-iteration leg", file=sys.stderr, flush=True)
         lr = bench_lowrank(cfz, torch, dev)
