@@ -517,6 +517,33 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 3 * 2 * src.numel() * 2 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
     del dst
+    # the same copy kernel at the compress launch's traffic (read + write = its algorithmic
+    # bytes), 57 launches replayed from a graph: what a launch of that size can reach
+    lay_elems = int(bc * n * 2) // 4  # 2-byte elements: half the bytes read, half written
+    lay_elems -= lay_elems % 8
+    flat = X.reshape(-1)
+    srcs = torch.empty(57 * lay_elems, dtype=torch.bfloat16, device=dev)
+    for o in range(0, srcs.numel(), flat.numel()):  # activation data, not an empty buffer
+        k = min(flat.numel(), srcs.numel() - o)
+        srcs[o:o + k].copy_(flat[:k])
+    srcs = srcs.view(57, lay_elems)
+    dsts = torch.empty_like(srcs)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    gcopy = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gcopy, stream=cap):
+        for i in range(57):
+            cfz.cfz_stream_copy(srcs[i], dsts[i], stream=cap)
+    torch.cuda.synchronize()
+    gcopy.replay()
+    torch.cuda.synchronize()
+    ce[0].record()
+    for _ in range(3):
+        gcopy.replay()
+    ce[1].record()
+    torch.cuda.synchronize()
+    layer_copy_gbs = 3 * 57 * 2 * lay_elems * 2 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
+    del dsts, srcs, gcopy
 
     workload = "flux-share-57x2x1024x3072-int4-g64-delta"
     traffic = load_traffic("compress", f"{workload}/{args.launch}")
@@ -553,6 +580,7 @@ def main():
             "decode": {"avg_launch_us": round(avg_dec * 1e6, 3), "GB/s": round(dec_gbs, 1),
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": bd},
             "stream_copy_ceiling_GB/s": round(copy_gbs, 1),
+            "stream_copy_at_compress_launch_size_GB/s": round(layer_copy_gbs, 1),
         },
         "other_launch_granularities": other_modes,
         "bf16_state": bf16_state,
