@@ -360,6 +360,40 @@ def test_cogvideox_full_size_sampled_rows(bits, group):
     _batched_rows_parity("cogvideox", bits, group, sp.steps, sl, f"cogvideox b{bits}")
 
 
+@pytest.mark.parametrize("bits,group", [(4, 64), (2, 32)])
+def test_cogvideox_full_size_per_layer_launches(bits, group):
+    """CogVideoX-2b share in the benchmark's launch configuration: 30 layers x {K, V} of
+    4388 x 1920, one grouped compress and one grouped decode launch per layer, 49 compressed
+    steps; layers 0 and 29 (tensors 0, 1, 58, 59) compared with the oracle every step."""
+    sp = SPECS["cogvideox"]
+    st = AR1Stream.from_spec(sp, seed=2, device=DEV)
+    picks = [0, 1, 58, 59]
+    say(f"[gpu] cogvideox per-layer launches int{bits} g{group}, tensors {picks}")
+    x = st.next()
+    n = sp.rows * sp.cols
+    gs = [cfz.Sender(sp.rows, sp.cols, bits, group, x0=x[i].contiguous()) for i in range(sp.tensors)]
+    gr = [cfz.Receiver(sp.rows, sp.cols, bits, group, x0=x[i].contiguous())
+          for i in range(sp.tensors)]
+    os_ = {i: oracle.Sender(n, bits, group, oracle.DELTA, x0=u16(x[i])) for i in picks}
+    or_ = {i: oracle.Receiver(n, bits, group, x0=u16(x[i])) for i in picks}
+    for t in range(1, sp.steps):
+        x = st.next()
+        for l in range(sp.tensors // 2):
+            pair = (2 * l, 2 * l + 1)
+            cfz.cfz_compress_group([gs[k].handle for k in pair], [x[k].contiguous() for k in pair],
+                                   [gs[k].codes for k in pair], [gs[k].scales for k in pair])
+            cfz.cfz_decompress_group([gr[k].handle for k in pair], [gs[k].codes for k in pair],
+                                     [gs[k].scales for k in pair])
+        torch.cuda.synchronize()
+        for i in picks:
+            oc, osc = os_[i].compress(u16(x[i]))
+            or_[i].decompress(oc, osc)
+            _compare_step(f"cogvideox t{t} tensor {i}", gs[i], gr[i], gs[i].codes, gs[i].scales,
+                          os_[i], or_[i], oc, osc)
+    for h in gs + gr:
+        h.close()
+
+
 def test_graph_replay_matches_oracle_every_replay():
     """The benchmark replays captured per-tensor launches; every replay must advance the state
     exactly like an eager step (checked against the oracle after each replay, with eager
