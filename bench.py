@@ -158,6 +158,7 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
             "achieved_GB/s_single_read": round(alg / t / 1e9, 1),
             "frac_hbm_peak_single_read": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
             "A_passes": 2 * T + 1,
+            "achieved_GB/s_all_passes": round((2 * T + 1) * batch * 2 * m * n / t / 1e9, 1),
             "useful_TFLOP/s": round(useful_flop / t / 1e12, 2),
             "mfma_TFLOP/s_executed": round(2 * useful_flop / t / 1e12, 2)}
         del ws
