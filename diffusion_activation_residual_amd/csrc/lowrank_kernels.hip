@@ -562,36 +562,59 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
     const int lane = threadIdx.x;
     constexpr int PER = RP * RP / kCholThreads;
 
-    // 1. sum the partials, entries in flight together, partials in a fixed order
+    // 1. sum the partials in a fixed order.  Every load is issued before the
+    //    first add waits: QU partials per round (all the lane's entries of each),
+    //    and in pass 2 R1^-1 alongside.
     const double *part = (const double *)(wsb + off_gram);
+    const bool col = lane < RP;
+    const int lc = col ? lane : 0;
+    double s1v[PER];
+    if (pass == 2) {
+        const double *r1inv = (const double *)(wsb + off_r1inv);
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            s1v[e] = r1inv[lane + kCholThreads * e];
+    }
+    constexpr int QU = PER >= 16 ? 2 : 32 / PER;
     double sum[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         sum[e] = 0.0;
-    for (int q = 0; q < gram_blocks; ++q)
+    for (int q0 = 0; q0 < gram_blocks; q0 += QU) {
+        double v[QU][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            sum[e] += part[(size_t)q * RP * RP + lane + kCholThreads * e];
+        for (int j = 0; j < QU; ++j) {  // past the last partial: re-read it, add nothing
+            const int q = q0 + j < gram_blocks ? q0 + j : gram_blocks - 1;
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                v[j][e] = part[(size_t)q * RP * RP + lane + kCholThreads * e];
+        }
+#pragma unroll
+        for (int j = 0; j < QU; ++j)
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                sum[e] += q0 + j < gram_blocks ? v[j][e] : 0.0;
+    }
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         const int idx = lane + kCholThreads * e;
         G[idx / RP][idx % RP] = sum[e];
     }
-    if (pass == 2) {
-        const double *r1inv = (const double *)(wsb + off_r1inv);
-        for (int e = lane; e < RP * RP; e += kCholThreads)
-            S1[e / RP][e % RP] = r1inv[e];
-    }
+    if (pass == 2)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + kCholThreads * e;
+            S1[idx / RP][idx % RP] = s1v[e];
+        }
     __syncthreads();
     double tr = 0.0;
-    for (int k = 0; k < r; ++k)
-        tr += G[k][k];
+#pragma unroll
+    for (int k = 0; k < RP; ++k)
+        tr += k < r ? G[k][k] : 0.0;
     const double tol = 1e-13 * tr / r;
 
     // 2. factorisation: gc[i] = G[i][lane] for i <= lane, overwritten by R[i][lane].
     //    Steps k >= r only see zero padding; they run with a zero pivot and change nothing.
-    const bool col = lane < RP;
-    const int lc = col ? lane : 0;
     uint32_t dead = 0;
     {
         double gc[RP];
