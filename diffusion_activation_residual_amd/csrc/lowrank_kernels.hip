@@ -625,17 +625,26 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
         for (int k = 0; k < RP; ++k) {
             const double dkk = readlane_f64(gc[k], k);
             const bool bad = k >= r || !(dkk > tol) || !isfinite(dkk);
-            const double rkk = bad ? 0.0 : sqrt(dkk);
-            const double inv = bad ? 0.0 : 1.0 / rkk;
-            dead |= bad ? (1u << k) : 0u;
-            const double rk = (lane == k) ? rkk : (lane > k ? gc[k] * inv : 0.0);
-            gc[k] = rk;
+            // 1 / sqrt(pivot): the hardware estimate and two Newton steps (within
+            // about an ulp), a third of the latency of a rounded sqrt and divide on
+            // the one chain every step waits for
+            const double d = bad ? 1.0 : dkk;
+            double y = __builtin_amdgcn_rsq(d);
 #pragma unroll
-            for (int i = k + 1; i < RP; ++i) {
-                const double rki = readlane_f64(rk, i);
-                if (lane >= i)
-                    gc[i] = fma(-rki, rk, gc[i]);
-            }
+            for (int it = 0; it < 2; ++it)
+                y = fma(0.5 * y, fma(-d * y, y, 1.0), y);
+            const double inv = bad ? 0.0 : y;
+            dead |= bad ? (1u << k) : 0u;
+            // R[k][lane] = G[k][lane] / R[k][k]; on the diagonal that is the pivot
+            // times its inverse square root, R[k][k] itself
+            const double rk = gc[k] * (lane >= k ? inv : 0.0);
+            gc[k] = rk;
+            // every lane updates: below the diagonal (i > lane) the values stay
+            // finite and are only ever multiplied by zero or dropped, so no lane
+            // mask is needed
+#pragma unroll
+            for (int i = k + 1; i < RP; ++i)
+                gc[i] = fma(-readlane_f64(rk, i), rk, gc[i]);
         }
         // a dropped column has a zero R column as well; pad columns (>= r) are zero
         const bool zero_col = !col || ((dead >> lc) & 1u);
@@ -649,15 +658,19 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
         rdiag[lc] = ((dead >> lc) & 1u) ? 0.0 : 1.0 / Rs[lc][lc];
     __syncthreads();
 
-    // 3. inverse: x[i] = (R^-1)[i][lane]
+    // 3. inverse: x[i] = (R^-1)[i][lane], bottom row first.  Each sum runs from
+    //    the far end, so x[i + 1], the value just computed, enters last and the
+    //    rows' sums overlap.
     double x[RP];
 #pragma unroll
     for (int i = RP - 1; i >= 0; --i) {
         double s = 0.0;
 #pragma unroll
-        for (int k = i + 1; k < RP; ++k)
+        for (int k = RP - 1; k > i; --k)
             s = fma(Rs[i][k], x[k], s);
-        x[i] = (i == lane) ? rdiag[i] : (i < lane ? -s * rdiag[i] : 0.0);
+        // (delta - s) / R[i][i]: below the diagonal every x[k] in s is zero, so
+        // one expression covers all three cases without a branch
+        x[i] = ((i == lane ? 1.0 : 0.0) - s) * rdiag[i];
     }
 
     double *r1 = (double *)(wsb + off_r1), *r1inv = (double *)(wsb + off_r1inv);
@@ -672,23 +685,37 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
         }
         return;
     }
-    // 4. pass 2: column lane of R2 R1 and of R1^-1 R2^-1
+    // 4. pass 2: column lane of R2 R1 and of R1^-1 R2^-1, four rows at a time
+    //    (their sums interleave), the group's stores after its sums
     float *ru = ru_out ? ru_out + (size_t)b * r * r : nullptr;
+    const bool ru_col = ru != nullptr && lane < r;
     double r1c[RP];
 #pragma unroll
     for (int k = 0; k < RP; ++k)
         r1c[k] = r1[k * RP + lane];
+    constexpr int IG = 4;
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
-        double sw = 0.0, si = 0.0;
+    for (int i0 = 0; i0 < RP; i0 += IG) {
+        double sw[IG], si[IG];
 #pragma unroll
-        for (int k = i; k < RP; ++k) {
-            sw = fma(Rs[i][k], r1c[k], sw);
-            si = fma(S1[i][k], x[k], si);
+        for (int ii = 0; ii < IG; ++ii) {
+            const int i = i0 + ii;
+            sw[ii] = 0.0;
+            si[ii] = 0.0;
+#pragma unroll
+            for (int k = i; k < RP; ++k) {
+                sw[ii] = fma(Rs[i][k], r1c[k], sw[ii]);
+                si[ii] = fma(S1[i][k], x[k], si[ii]);
+            }
         }
-        rinv[i * RP + lane] = si;
-        if (ru && i < r && lane < r)
-            ru[i * r + lane] = (float)sw;
+#pragma unroll
+        for (int ii = 0; ii < IG; ++ii)
+            rinv[(i0 + ii) * RP + lane] = si[ii];
+        if (ru_col)
+#pragma unroll
+            for (int ii = 0; ii < IG; ++ii)
+                if (i0 + ii < r)
+                    ru[(i0 + ii) * r + lane] = (float)sw[ii];
     }
 }
 
