@@ -276,7 +276,9 @@ lr_aq_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_
 
 // ------------------------------------------------------------------ Z = A^T Y
 
-constexpr int kAtyCols = 64;  // columns of A per work-group (4 waves x 16)
+constexpr int kAtyWaves = 8;                 // waves per work-group, 16 columns each
+constexpr int kAtyThreads = 64 * kAtyWaves;
+constexpr int kAtyCols = 16 * kAtyWaves;     // columns of A per work-group
 
 constexpr int kAtyRows = 64;  // rows of A per pipeline step (two 32-row MFMA k steps)
 
@@ -294,14 +296,16 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p)
         (__attribute__((address_space(3))) i16x4 *)(p));
 }
 
-// One work-group: 64 columns of A (wave w owns columns 16w..16w+15) against all
-// rows.  Each 64-row slab of A is loaded with coalesced 16-byte loads, stored in
+// One work-group: kAtyCols = 128 columns of A (wave w owns columns 16w..16w+15)
+// against all rows; each row of a slab is then one 256-byte piece (64-column
+// work-groups, reading 128-byte pieces 6 KB apart, took 2-4% longer per call).
+// Each 64-row slab of A is loaded with coalesced 16-byte loads, stored in
 // LDS as it is (one 16-byte store per load) and read back with the transposing
 // LDS load, so that a lane's MFMA operand (8 consecutive rows of one column) is
 // two 8-byte reads.  Same pipeline as A Q: slabs kPipe steps ahead in static
 // register stages, Y tiles one step ahead, double-buffered LDS.
 template <int RP>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kAtyThreads)
 lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
               size_t layer_bytes, size_t off_yops, size_t off_out, int64_t mp, int blocks_per_mat)
 {
@@ -312,16 +316,19 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     const bf16x8 *ylo = yhi + (mp / 8) * RP;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)b * m * n, (uint32_t)(m * n * 2));
 
-    constexpr int SCOL = kAtyCols + 8;             // padded slab row: 144 B, rows 4 banks apart
+    constexpr int SCOL = kAtyCols + 8;             // padded slab row: rows 4 banks apart
     __shared__ __attribute__((aligned(16))) uint16_t sa[2][kAtyRows][SCOL];
     __shared__ bf16x8 sy[2][2][kAtyRows / 8][RP];  // [buffer][hi, lo][k block][column]
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
-    // loader role: thread t loads rows t/8 and t/8 + 32 of the slab, columns 8*(t%8) .. +7
-    const int trow = threadIdx.x / 8, tcc = threadIdx.x % 8;
+    // loader role: thread t loads rows t/C and t/C + 32 of the slab, columns 8*(t%C) .. +7
+    // (C = kAtyCols / 8 chunks of 16 bytes per slab row)
+    constexpr int C = kAtyCols / 8;
+    static_assert(kAtyThreads / C == 32, "two loads per thread cover the 64-row slab");
+    const int trow = threadIdx.x / C, tcc = threadIdx.x % C;
     const int64_t tcol = (int64_t)blk * kAtyCols + 8 * tcc;
     constexpr int YE = 2 * (kAtyRows / 8) * RP;
-    constexpr int YPT = (YE + kThreads - 1) / kThreads;
+    constexpr int YPT = (YE + kAtyThreads - 1) / kAtyThreads;
     const int64_t last_slab = mp - kAtyRows;       // Y loads past the end re-read a valid slab
 
     auto load_a = [&](int64_t i0, u32x4 (&av)[2]) {
@@ -336,7 +343,7 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
         const int64_t kt = (i0 < last_slab ? i0 : last_slab) / 8;
 #pragma unroll
         for (int p = 0; p < YPT; ++p) {
-            const int e = threadIdx.x + p * kThreads;
+            const int e = threadIdx.x + p * kAtyThreads;
             const int ee = e < YE ? e : 0;
             const int hl = ee / ((kAtyRows / 8) * RP), rem = ee % ((kAtyRows / 8) * RP);
             const int kb = rem / RP, c = rem % RP;
@@ -349,7 +356,7 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
             *(u32x4 *)&sa[buf][trow + 32 * h][8 * tcc] = av[h];
 #pragma unroll
         for (int p = 0; p < YPT; ++p) {
-            const int e = threadIdx.x + p * kThreads;
+            const int e = threadIdx.x + p * kAtyThreads;
             if (e < YE)
                 (&sy[buf][0][0][0])[e] = yv[p];
         }
@@ -880,7 +887,7 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
                            dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
                            Ly.off_qops, Ly.off_yops, Ly.mp, Ly.np, aq_blocks);
         hipLaunchKernelGGL((lr_aty_kernel<RP>), dim3((unsigned)(aty_blocks * a.batch)),
-                           dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
+                           dim3(kAtyThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
                            Ly.off_yops, Ly.off_mf, Ly.mp, aty_blocks);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
