@@ -17,8 +17,9 @@
 //                           bf16(Y') too (8 or 10 bytes per element, HBM bound).  The
 //                           rank-r product is a contraction over r <= 32, evaluated as
 //                           U (V R_U^T)^T on v_mfma_f32_16x16x4_f32: a work-group owns
-//                           a 256 x 256 block, forms its columns' rows of V R_U^T once
-//                           in registers and streams the block's rows of Y and U.
+//                           256 columns of 256 rows (1024 at r = 32), forms its columns'
+//                           rows of V R_U^T once in registers and streams the block's
+//                           rows of Y and U.
 //                           Sender and receiver run the same kernel on the same factors,
 //                           so their reconstructions agree bit for bit.
 
@@ -34,7 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kUpdRows = 256;  // rows of Y per work-group of the update (16 blocks of 16)
+constexpr int kUpdRows = 256;  // rows of Y per work-group of the update at r <= 16
 constexpr int kUpdCols = 256;  // columns per work-group (each wave: 64 = 4 tiles of 16)
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -253,20 +254,29 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
     }
 }
 
+// Rows per work-group: each work-group first forms its columns' rows of V R_U^T
+// (r x r work per column), so at r = 32 taller blocks amortise that better
+// (1024 rows: 334 / 408 us per sender / receiver call at 57 x 1024 x 3072,
+// against 423 / 493 us with 256); at r <= 16, 256 rows is fastest.
+template <int RP>
+constexpr int upd_rows() { return RP == 32 ? 4 * kUpdRows : kUpdRows; }
+
 template <int RP>
 hipError_t update_rp(int64_t batch, int64_t m, int64_t n, int r, const float *U, const float *V,
                      const float *RU, float sign, float *Y, uint16_t *xhat, hipStream_t st)
 {
-    const int rg = (int)((m + kUpdRows - 1) / kUpdRows);
+    constexpr int ROWS = upd_rows<RP>();
+    const int rg = (int)((m + ROWS - 1) / ROWS);
     const int cg = (int)((n + kUpdCols - 1) / kUpdCols);
     const int64_t blocks = batch * rg * cg;
-    hipLaunchKernelGGL((lr_ef_update_kernel<RP, kUpdRows>), dim3((unsigned)blocks), dim3(kThreads),
+    hipLaunchKernelGGL((lr_ef_update_kernel<RP, ROWS>), dim3((unsigned)blocks), dim3(kThreads),
                        0, st, m, n, r, U, V, RU, sign, Y, xhat, rg, cg);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// The largest grid any rank class launches (the shortest blocks).
 int64_t lowrank_ef_update_blocks(int64_t batch, int64_t m, int64_t n)
 {
     return batch * ((m + kUpdRows - 1) / kUpdRows) * ((n + kUpdCols - 1) / kUpdCols);

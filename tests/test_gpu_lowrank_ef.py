@@ -136,9 +136,10 @@ def _run(batch, m, n, r, T, steps, check, seed=0, warm_start=False, rank=16):
 
 @pytest.mark.parametrize("batch,m,n,r,T", [(1, 256, 384, 8, 2), (3, 200, 328, 5, 1),
                                            (2, 130, 264, 16, 2), (1, 64, 512, 32, 0),
-                                           (2, 96, 136, 1, 3)])
+                                           (2, 96, 136, 1, 3), (1, 1100, 264, 32, 1)])
 def test_teacher_forced_steps(batch, m, n, r, T):
-    """Several tiles and ragged edges of the 64 x 128 update tile; every rank class."""
+    """Several tiles and ragged edges of the update's blocks (256 columns of 256 rows, or
+    1024 rows at r = 32); every rank class."""
     _run(batch, m, n, r, T, 4, range(batch), seed=batch * 7 + r)
 
 
