@@ -449,8 +449,9 @@ def main():
             cfz.cfz_state_destroy(h)
         t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
         t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+        per_step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
         return {"elapsed": elapsed, "t_comp": t_comp, "t_dec": t_dec, "launches": launches,
-                "tensors_per_launch": T / launches}
+                "tensors_per_launch": T / launches, "per_step_ms": per_step_ms}
 
     print(f"[bench] timing {K} steps ({args.launch} launches)", file=sys.stderr, flush=True)
     res = run_mode(args.launch, K, W, not args.no_graph)
@@ -556,6 +557,10 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(elapsed / K * 1e3, 4),
+        "step_ms_events": {  # compress + decode of one step, HIP events on the launch stream
+            "median": round(res["per_step_ms"][len(res["per_step_ms"]) // 2], 4),
+            "min": round(res["per_step_ms"][0], 4),
+            "max": round(res["per_step_ms"][-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
