@@ -203,6 +203,94 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
                 "bytes_per_elem": 10}}
 
 
+def bench_ef_modes(cfz, torch, X, slots, rows, cols, steps=10):
+    """The three error-feedback readings on the FLUX share at int4 g64 and int2 g32, one
+    grouped compress and one grouped decode launch per layer from HIP graphs, steps
+    1..steps+1 in order (the first untimed): kernel rates against each mode's algorithmic
+    bytes, and the receiver's relative error ||base - x|| / ||x|| after the last step."""
+    T = X.shape[1]
+    out = {"workload": f"flux-share {T} tensors of {rows}x{cols}, one grouped launch per layer "
+                       "(K and V), replayed from HIP graphs", "steps": steps}
+    for bits, group in ((4, 64), (2, 32)):
+        out[f"int{bits}_g{group}"] = _ef_modes_one(cfz, torch, X, slots, rows, cols, bits, group,
+                                                   steps)
+        torch.cuda.empty_cache()
+    return out
+
+
+def _ef_modes_one(cfz, torch, X, slots, rows, cols, bits, group, steps):
+    T, n = X.shape[1], X.shape[2]
+    dev = X.device
+    codes = torch.empty((T, n * bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, n // group), dtype=torch.float32, device=dev)
+    rbase = torch.empty((T, n), dtype=torch.float32, device=dev)
+    layers = [(2 * l, 2 * l + 1) for l in range(T // 2)]
+    names = {cfz.CFZ_EF_DELTA: "delta", cfz.CFZ_EF_LITERAL: "literal", cfz.CFZ_EF_OFF: "off"}
+    out = {}
+    for mode in (cfz.CFZ_EF_DELTA, cfz.CFZ_EF_LITERAL, cfz.CFZ_EF_OFF):
+        sd = cfz.make_desc(rows, cols, bits, group, mode, cfz.CFZ_SENDER)
+        rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
+        prev = torch.empty((T, n), dtype=torch.bfloat16, device=dev) if mode == cfz.CFZ_EF_DELTA else None
+        sbase = torch.empty((T, n), dtype=torch.float32, device=dev) if mode != cfz.CFZ_EF_DELTA else None
+        err = torch.empty((T, n), dtype=torch.float32, device=dev) if mode != cfz.CFZ_EF_OFF else None
+
+        def states():
+            return ([cfz.cfz_state_create(sd, prev=None if prev is None else prev[i],
+                                          base=None if sbase is None else sbase[i],
+                                          err=None if err is None else err[i], x0=X[0, i])
+                     for i in range(T)],
+                    [cfz.cfz_state_create(rd, base=rbase[i], x0=X[0, i]) for i in range(T)])
+
+        snd, rcv = states()
+        slot_of = [1 + k % (slots - 1) for k in range(steps + 1)]
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        gc = {}
+        for s_ in sorted(set(slot_of)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for c in layers:
+                    cfz.cfz_compress_group([snd[i] for i in c], [X[s_, i] for i in c],
+                                           [codes[i] for i in c], [scales[i] for i in c])
+            gc[s_] = g
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd, stream=cap):
+            for c in layers:
+                cfz.cfz_decompress_group([rcv[i] for i in c], [codes[i] for i in c],
+                                         [scales[i] for i in c])
+        torch.cuda.synchronize()
+        for h in snd + rcv:  # capture only recorded the launches; start from a fresh warm-up
+            cfz.cfz_state_destroy(h)
+        snd[:], rcv[:] = states()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
+        for k in range(steps + 1):
+            ev[k][0].record()
+            gc[slot_of[k]].replay()
+            ev[k][1].record()
+            gd.replay()
+            ev[k][2].record()
+        torch.cuda.synchronize()
+        tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / (steps * len(layers))
+        td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / (steps * len(layers))
+        x_last = X[slot_of[-1]].float()
+        rel = (torch.linalg.vector_norm(rbase - x_last) / torch.linalg.vector_norm(x_last)).item()
+        for h in snd + rcv:
+            cfz.cfz_state_destroy(h)
+        del gc, gd
+        bc, bd = algorithmic_bytes(bits, group, names[mode])
+        out[names[mode]] = {
+            "compress": {"avg_launch_us": round(tc * 1e6, 3),
+                         "GB/s": round(bc * 2 * n / tc / 1e9, 1),
+                         "frac_hbm_peak": round(bc * 2 * n / tc / 1e9 / HBM_PEAK_GBS, 4),
+                         "bytes_per_elem": bc},
+            "decode": {"avg_launch_us": round(td * 1e6, 3),
+                       "GB/s": round(bd * 2 * n / td / 1e9, 1),
+                       "frac_hbm_peak": round(bd * 2 * n / td / 1e9 / HBM_PEAK_GBS, 4)},
+            "activation_GB/s": round(2 * n * T / ((tc + td) * len(layers)) / 1e9, 2),
+            "receiver_rel_error_last_step": float(f"{rel:.4g}")}
+    return out
+
+
 def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
     """CogVideoX-2b share at sequence-parallel degree 4: 30 layers x {K, V} of 4388 x 1920
     bf16 (AR(1), alpha 0.97), DELTA, one grouped compress and one grouped decode launch per
@@ -323,6 +411,8 @@ def main():
     ap.add_argument("--launch", choices=("layer", "tensor", "step"), default="layer",
                     help="tensors per launch: K+V of a layer (default), one, or the whole step")
     ap.add_argument("--no-modes", action="store_true", help="skip the other launch granularities")
+    ap.add_argument("--no-ef-modes", action="store_true",
+                    help="skip the LITERAL / OFF error-feedback readings leg")
     ap.add_argument("--no-bf16-state", action="store_true",
                     help="skip the leg with the carried error and base held in bf16")
     ap.add_argument("--pool", type=int, default=29,
@@ -592,6 +682,10 @@ def main():
         "bf16_state": bf16_state,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
     }
+    if not args.no_ef_modes:
+        print("[bench] error-feedback readings leg", file=sys.stderr, flush=True)
+        line["ef_modes"] = bench_ef_modes(cfz, torch, X, slots, rows, cols, steps=min(K, 10))
+        torch.cuda.empty_cache()
     if not args.no_batched:
         print("[bench] batched int2 leg", file=sys.stderr, flush=True)
         line["batched_int2_g32"] = bench_batched(cfz, torch, X, slots, T * rows, cols, 2, 32,
