@@ -3,7 +3,9 @@
 Every step of the codec and of the subspace iteration runs in the HIP kernels
 of ``libcfz.so``; this module converts torch tensors into raw device pointers
 and the current HIP stream, calls the C entry point of the same name, and
-turns a non-OK status into ``CfzError``.  torch supplies device memory and
+turns a non-OK status into ``CfzError``.  Because it sees tensor sizes, which
+the C ABI cannot, it also refuses (``ValueError``, before any device work) a
+tensor smaller than the call would touch.  torch supplies device memory and
 streams, nothing else.  There is no fallback: if the library is not built,
 importing this module raises.
 """
@@ -109,6 +111,53 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# handle -> sizes its calls touch (elements, codes bytes, scales bytes), for the size checks
+_sizes = {}
+
+
+def _need(t, nbytes, what):
+    """Raise before any device work when a tensor is smaller than the call will touch (raw
+    integer pointers are the caller's responsibility, as in C)."""
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: tensor holds {have} bytes, the call touches {nbytes}")
+
+
+def _record(handle, desc):
+    n = max(desc.rows * desc.cols, 0)
+    _sizes[handle] = (n, _lib.cfz_codes_bytes(C.byref(desc)), _lib.cfz_scales_bytes(C.byref(desc)))
+
+
+def _check_state_buffers(desc, prev, base, err, x0=None):
+    n = max(desc.rows * desc.cols, 0)
+    w = 2 if desc.state_dtype == CFZ_STATE_BF16 else 4
+    _need(prev, 2 * n, "prev")
+    _need(base, w * n, "base")
+    _need(err, w * n, "err")
+    _need(x0, 2 * n, "x0")
+
+
+def _check_payload(handle, x=None, codes=None, scales=None, xhat=None):
+    if handle not in _sizes:
+        return
+    n, cb, sb = _sizes[handle]
+    _need(x, 2 * n, "x")
+    _need(codes, cb, "codes")
+    _need(scales, sb, "scales")
+    _need(xhat, 2 * n, "xhat")
+
+
+def _check_lowrank(batch, m, n, r, A=None, Q0=None, U=None, V=None, RU=None):
+    b, m, n, r = (max(int(v), 0) for v in (batch, m, n, r))
+    _need(A, 2 * b * m * n, "A")
+    _need(Q0, 4 * b * n * r, "Q0")
+    _need(U, 4 * b * m * r, "U")
+    _need(V, 4 * b * n * r, "V")
+    _need(RU, 4 * b * r * r, "RU")
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -152,22 +201,27 @@ def cfz_scales_bytes(desc: cfz_desc) -> int:
 
 
 def cfz_state_create(desc: cfz_desc, prev=None, base=None, err=None, x0=None, stream=None):
+    _check_state_buffers(desc, prev, base, err, x0)
     bufs = cfz_buffers(_bf16_ptr(prev), _ptr(base), _ptr(err))
     out = C.c_void_p()
     _check(_lib.cfz_state_create(C.byref(desc), C.byref(bufs), _bf16_ptr(x0), _stream(stream),
                                  C.byref(out)), "cfz_state_create")
+    _record(out.value, desc)
     return out.value
 
 
 def cfz_state_resume(desc: cfz_desc, prev=None, base=None, err=None, steps=0):
+    _check_state_buffers(desc, prev, base, err)
     bufs = cfz_buffers(_bf16_ptr(prev), _ptr(base), _ptr(err))
     out = C.c_void_p()
     _check(_lib.cfz_state_resume(C.byref(desc), C.byref(bufs), steps, C.byref(out)),
            "cfz_state_resume")
+    _record(out.value, desc)
     return out.value
 
 
 def cfz_state_destroy(handle) -> None:
+    _sizes.pop(handle, None)
     _check(_lib.cfz_state_destroy(handle), "cfz_state_destroy")
 
 
@@ -176,11 +230,13 @@ def cfz_state_steps(handle) -> int:
 
 
 def cfz_compress(handle, x, codes, scales, stream=None) -> None:
+    _check_payload(handle, x=x, codes=codes, scales=scales)
     _check(_lib.cfz_compress(handle, _bf16_ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
            "cfz_compress")
 
 
 def cfz_decompress(handle, codes, scales, xhat=None, stream=None) -> None:
+    _check_payload(handle, codes=codes, scales=scales, xhat=xhat)
     _check(_lib.cfz_decompress(handle, _ptr(codes), _ptr(scales), _bf16_ptr(xhat),
                                _stream(stream)), "cfz_decompress")
 
@@ -197,6 +253,8 @@ def cfz_compress_group(handles, xs, codes, scales, stream=None) -> None:
     n = len(handles)
     if not (len(xs) == len(codes) == len(scales) == n):
         raise ValueError("all lists must have one entry per state")
+    for i in range(n):
+        _check_payload(handles[i], x=xs[i], codes=codes[i], scales=scales[i])
     _check(_lib.cfz_compress_group(n, _ptr_array(handles, lambda h: h), _ptr_array(xs, _bf16_ptr),
                                    _ptr_array(codes), _ptr_array(scales), _stream(stream)),
            "cfz_compress_group")
@@ -206,6 +264,9 @@ def cfz_decompress_group(handles, codes, scales, xhats=None, stream=None) -> Non
     n = len(handles)
     if not (len(codes) == len(scales) == n) or (xhats is not None and len(xhats) != n):
         raise ValueError("all lists must have one entry per state")
+    for i in range(n):
+        _check_payload(handles[i], codes=codes[i], scales=scales[i],
+                       xhat=None if xhats is None else xhats[i])
     xa = None if xhats is None else _ptr_array(xhats, _bf16_ptr)
     _check(_lib.cfz_decompress_group(n, _ptr_array(handles, lambda h: h), _ptr_array(codes),
                                      _ptr_array(scales), xa, _stream(stream)),
@@ -219,6 +280,8 @@ def cfz_lowrank_workspace_bytes(batch, m, n, r) -> int:
 def cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, workspace, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check_lowrank(batch, m, n, r, A, Q0, U, V, RU)
+    _need(workspace, ws_bytes, "workspace")
     _check(_lib.cfz_lowrank(batch, m, n, r, T, _bf16_ptr(A), _ptr(Q0), _ptr(U), _ptr(V),
                             _ptr(RU), _ptr(workspace), ws_bytes, _stream(stream)), "cfz_lowrank")
 
@@ -228,6 +291,11 @@ def cfz_lowrank_ef_workspace_bytes(batch, m, n, r) -> int:
 
 
 def cfz_lowrank_ef_warmup(count, x0=None, prev=None, err=None, base=None, stream=None) -> None:
+    c = max(int(count), 0)
+    _need(x0, 2 * c, "x0")
+    _need(prev, 2 * c, "prev")
+    _need(err, 4 * c, "err")
+    _need(base, 4 * c, "base")
     _check(_lib.cfz_lowrank_ef_warmup(count, _bf16_ptr(x0), _bf16_ptr(prev), _ptr(err), _ptr(base),
                                       _stream(stream)), "cfz_lowrank_ef_warmup")
 
@@ -236,12 +304,22 @@ def cfz_lowrank_ef_compress(batch, m, n, r, T, x, prev, err, Q0, U, V, RU, works
                             ws_bytes=None, stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check_lowrank(batch, m, n, r, None, Q0, U, V, RU)
+    c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need(x, 2 * c, "x")
+    _need(prev, 2 * c, "prev")
+    _need(err, 4 * c, "err")
+    _need(workspace, ws_bytes, "workspace")
     _check(_lib.cfz_lowrank_ef_compress(batch, m, n, r, T, _bf16_ptr(x), _bf16_ptr(prev), _ptr(err),
                                         _ptr(Q0), _ptr(U), _ptr(V), _ptr(RU), _ptr(workspace),
                                         ws_bytes, _stream(stream)), "cfz_lowrank_ef_compress")
 
 
 def cfz_lowrank_ef_decompress(batch, m, n, r, U, V, RU, base, xhat=None, stream=None) -> None:
+    _check_lowrank(batch, m, n, r, None, None, U, V, RU)
+    c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need(base, 4 * c, "base")
+    _need(xhat, 2 * c, "xhat")
     _check(_lib.cfz_lowrank_ef_decompress(batch, m, n, r, _ptr(U), _ptr(V), _ptr(RU), _ptr(base),
                                           _bf16_ptr(xhat), _stream(stream)),
            "cfz_lowrank_ef_decompress")
@@ -250,6 +328,8 @@ def cfz_lowrank_ef_decompress(batch, m, n, r, U, V, RU, base, xhat=None, stream=
 def cfz_stream_copy(src, dst, nbytes=None, stream=None) -> None:
     if nbytes is None:
         nbytes = src.numel() * src.element_size()
+    _need(src, nbytes, "src")
+    _need(dst, nbytes, "dst")
     _check(_lib.cfz_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "cfz_stream_copy")
 
 

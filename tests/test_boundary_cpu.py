@@ -227,3 +227,62 @@ def test_group_validation_without_launching():
     finally:
         for h in (a, b, lit, rcv, half):
             cfz.cfz_state_destroy(h)
+
+
+def test_binding_rejects_undersized_tensors_before_any_launch():
+    """A tensor smaller than the call touches raises ValueError in the binding, on the host,
+    before anything reaches a device; raw integer pointers stay the caller's responsibility."""
+    import torch
+    n = 4 * 64
+    d = cfz.make_desc(4, 64)
+    with pytest.raises(ValueError, match="prev"):
+        cfz.cfz_state_create(d, prev=torch.empty(n - 1, dtype=torch.bfloat16), err=torch.empty(n))
+    half = cfz.make_desc(4, 64, state_dtype=cfz.CFZ_STATE_BF16)  # err and base: 2 bytes each
+    with pytest.raises(ValueError, match="err"):
+        cfz.cfz_state_create(half, prev=torch.empty(n, dtype=torch.bfloat16),
+                             err=torch.empty(n // 2 - 1))
+    snd = cfz.cfz_state_resume(d, prev=ALIGNED, err=ALIGNED)
+    rcv = cfz.cfz_state_resume(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER), base=ALIGNED)
+    try:
+        x = torch.empty(n, dtype=torch.bfloat16)
+        codes = torch.empty(n // 2, dtype=torch.uint8)
+        scales = torch.empty(n // 64)
+        with pytest.raises(ValueError, match="x:"):
+            cfz.cfz_compress(snd, x[: n - 8], codes, scales)
+        with pytest.raises(ValueError, match="codes"):
+            cfz.cfz_compress(snd, x, codes[:-1], scales)
+        with pytest.raises(ValueError, match="scales"):
+            cfz.cfz_decompress(rcv, codes, scales[:-1])
+        with pytest.raises(ValueError, match="xhat"):
+            cfz.cfz_decompress(rcv, codes, scales, x[:-1])
+        with pytest.raises(ValueError, match="scales"):
+            cfz.cfz_compress_group([snd], [x], [codes], [scales[:-1]])
+        with pytest.raises(ValueError, match="codes"):
+            cfz.cfz_decompress_group([rcv], [codes[:-2]], [scales])
+        # the right sizes pass this check and stop at the host-tensor check
+        with pytest.raises(ValueError, match="device tensors"):
+            cfz.cfz_compress(snd, x, codes, scales)
+    finally:
+        cfz.cfz_state_destroy(snd)
+        cfz.cfz_state_destroy(rcv)
+
+    b, m, nn, r = 2, 64, 128, 8
+    A = torch.empty(b * m * nn, dtype=torch.bfloat16)
+    Q0, U, V, RU = (torch.empty(b * nn * r), torch.empty(b * m * r), torch.empty(b * nn * r),
+                    torch.empty(b * r * r))
+    ws = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="A:"):
+        cfz.cfz_lowrank(b, m, nn, r, 1, A[:-1], Q0, U, V, RU, ws)
+    with pytest.raises(ValueError, match="RU"):
+        cfz.cfz_lowrank(b, m, nn, r, 1, A, Q0, U, V, RU[:-1], ws)
+    with pytest.raises(ValueError, match="workspace"):
+        cfz.cfz_lowrank(b, m, nn, r, 1, A, Q0, U, V, RU, ws, ws_bytes=17)
+    with pytest.raises(ValueError, match="err"):
+        cfz.cfz_lowrank_ef_compress(b, m, nn, r, 1, A, A, torch.empty(b * m * nn - 1), Q0, U, V,
+                                    RU, ws)
+    with pytest.raises(ValueError, match="base"):
+        cfz.cfz_lowrank_ef_decompress(b, m, nn, r, U, V, RU, torch.empty(b * m * nn - 1))
+    with pytest.raises(ValueError, match="prev"):
+        cfz.cfz_lowrank_ef_warmup(64, prev=torch.empty(63, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="dst"):
+        cfz.cfz_stream_copy(torch.empty(16, dtype=torch.uint8), torch.empty(15, dtype=torch.uint8))
