@@ -125,6 +125,19 @@ def _need(t, nbytes, what):
         raise ValueError(f"{what}: tensor holds {have} bytes, the call touches {nbytes}")
 
 
+def _need_dtype(t, dtypes, what):
+    """The same host-side guard for element types the kernels read as fp32 or bf16."""
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype not in dtypes:
+        names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{what}: {str(t.dtype).replace('torch.', '')} tensor, expected {names}")
+
+
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
 def _record(handle, desc):
     n = max(desc.rows * desc.cols, 0)
     _sizes[handle] = (n, _lib.cfz_codes_bytes(C.byref(desc)), _lib.cfz_scales_bytes(C.byref(desc)))
@@ -133,6 +146,9 @@ def _record(handle, desc):
 def _check_state_buffers(desc, prev, base, err, x0=None):
     n = max(desc.rows * desc.cols, 0)
     w = 2 if desc.state_dtype == CFZ_STATE_BF16 else 4
+    sdt = _BF16 if desc.state_dtype == CFZ_STATE_BF16 else _F32
+    _need_dtype(base, sdt, "base")
+    _need_dtype(err, sdt, "err")
     _need(prev, 2 * n, "prev")
     _need(base, w * n, "base")
     _need(err, w * n, "err")
@@ -143,6 +159,7 @@ def _check_payload(handle, x=None, codes=None, scales=None, xhat=None):
     if handle not in _sizes:
         return
     n, cb, sb = _sizes[handle]
+    _need_dtype(scales, _F32, "scales")
     _need(x, 2 * n, "x")
     _need(codes, cb, "codes")
     _need(scales, sb, "scales")
@@ -151,6 +168,8 @@ def _check_payload(handle, x=None, codes=None, scales=None, xhat=None):
 
 def _check_lowrank(batch, m, n, r, A=None, Q0=None, U=None, V=None, RU=None):
     b, m, n, r = (max(int(v), 0) for v in (batch, m, n, r))
+    for t, what in ((Q0, "Q0"), (U, "U"), (V, "V"), (RU, "RU")):
+        _need_dtype(t, _F32, what)
     _need(A, 2 * b * m * n, "A")
     _need(Q0, 4 * b * n * r, "Q0")
     _need(U, 4 * b * m * r, "U")
@@ -292,6 +311,8 @@ def cfz_lowrank_ef_workspace_bytes(batch, m, n, r) -> int:
 
 def cfz_lowrank_ef_warmup(count, x0=None, prev=None, err=None, base=None, stream=None) -> None:
     c = max(int(count), 0)
+    _need_dtype(err, _F32, "err")
+    _need_dtype(base, _F32, "base")
     _need(x0, 2 * c, "x0")
     _need(prev, 2 * c, "prev")
     _need(err, 4 * c, "err")
@@ -306,6 +327,7 @@ def cfz_lowrank_ef_compress(batch, m, n, r, T, x, prev, err, Q0, U, V, RU, works
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check_lowrank(batch, m, n, r, None, Q0, U, V, RU)
     c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need_dtype(err, _F32, "err")
     _need(x, 2 * c, "x")
     _need(prev, 2 * c, "prev")
     _need(err, 4 * c, "err")
@@ -318,6 +340,7 @@ def cfz_lowrank_ef_compress(batch, m, n, r, T, x, prev, err, Q0, U, V, RU, works
 def cfz_lowrank_ef_decompress(batch, m, n, r, U, V, RU, base, xhat=None, stream=None) -> None:
     _check_lowrank(batch, m, n, r, None, None, U, V, RU)
     c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need_dtype(base, _F32, "base")
     _need(base, 4 * c, "base")
     _need(xhat, 2 * c, "xhat")
     _check(_lib.cfz_lowrank_ef_decompress(batch, m, n, r, _ptr(U), _ptr(V), _ptr(RU), _ptr(base),

@@ -240,7 +240,7 @@ def test_binding_rejects_undersized_tensors_before_any_launch():
     half = cfz.make_desc(4, 64, state_dtype=cfz.CFZ_STATE_BF16)  # err and base: 2 bytes each
     with pytest.raises(ValueError, match="err"):
         cfz.cfz_state_create(half, prev=torch.empty(n, dtype=torch.bfloat16),
-                             err=torch.empty(n // 2 - 1))
+                             err=torch.empty(n - 1, dtype=torch.bfloat16))
     snd = cfz.cfz_state_resume(d, prev=ALIGNED, err=ALIGNED)
     rcv = cfz.cfz_state_resume(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER), base=ALIGNED)
     try:
@@ -286,3 +286,27 @@ def test_binding_rejects_undersized_tensors_before_any_launch():
         cfz.cfz_lowrank_ef_warmup(64, prev=torch.empty(63, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="dst"):
         cfz.cfz_stream_copy(torch.empty(16, dtype=torch.uint8), torch.empty(15, dtype=torch.uint8))
+
+
+def test_binding_rejects_wrong_element_types():
+    """fp32 buffers must be float32 and bf16-state buffers bfloat16 (or 16-bit patterns)."""
+    import torch
+    n = 4 * 64
+    half = cfz.make_desc(4, 64, state_dtype=cfz.CFZ_STATE_BF16)
+    with pytest.raises(TypeError, match="err"):
+        cfz.cfz_state_create(half, prev=torch.empty(n, dtype=torch.bfloat16), err=torch.empty(n))
+    with pytest.raises(TypeError, match="base"):
+        cfz.cfz_state_create(cfz.make_desc(4, 64, role=cfz.CFZ_RECEIVER),
+                             base=torch.empty(2 * n, dtype=torch.bfloat16))
+    snd = cfz.cfz_state_resume(cfz.make_desc(4, 64), prev=ALIGNED, err=ALIGNED)
+    try:
+        with pytest.raises(TypeError, match="scales"):
+            cfz.cfz_compress(snd, torch.empty(n, dtype=torch.bfloat16),
+                             torch.empty(n // 2, dtype=torch.uint8),
+                             torch.empty(n // 64, dtype=torch.float64))
+    finally:
+        cfz.cfz_state_destroy(snd)
+    with pytest.raises(TypeError, match="Q0"):
+        cfz.cfz_lowrank(1, 64, 128, 8, 1, torch.empty(64 * 128, dtype=torch.bfloat16),
+                        torch.empty(128 * 8, dtype=torch.float16), torch.empty(64 * 8),
+                        torch.empty(128 * 8), torch.empty(64), torch.empty(16, dtype=torch.uint8))
