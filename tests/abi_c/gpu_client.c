@@ -1,0 +1,192 @@
+/*
+ * Plain C11 client of include/cfz.h that runs the codec on the GPU: device
+ * memory from the HIP runtime API, every call through the C ABI of libcfz.so,
+ * no Python and no torch.  Each step's codes, scales, sender state, receiver
+ * base and bf16 output are copied back and compared byte for byte with the CPU
+ * oracle (oracle/libcfz_oracle.so, test infrastructure) run on the same inputs.
+ * Prints one line per case before its GPU work, and "OK" at the end.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "cfz.h"
+
+/* the oracle's entry points (oracle/cfz_oracle.c) */
+void oracle_warmup(int64_t n, int mode, int role, int state_bf16, const uint16_t *x0,
+                   uint16_t *prev, void *base, void *err);
+void oracle_compress(int64_t n, int bits, int group, int mode, int state_bf16, const uint16_t *x,
+                     uint16_t *prev, void *base, void *err, uint8_t *codes, float *scales);
+void oracle_decompress(int64_t n, int bits, int group, int state_bf16, const uint8_t *codes,
+                       const float *scales, void *base, uint16_t *xhat);
+
+#define FAIL(...)                                                        \
+    do {                                                                 \
+        fprintf(stderr, "%s:%d: ", __FILE__, __LINE__);                  \
+        fprintf(stderr, __VA_ARGS__);                                    \
+        fprintf(stderr, "\n");                                           \
+        return 1;                                                        \
+    } while (0)
+#define HIP(call)                                                        \
+    do {                                                                 \
+        hipError_t e_ = (call);                                          \
+        if (e_ != hipSuccess)                                            \
+            FAIL("%s: %s", #call, hipGetErrorString(e_));                \
+    } while (0)
+#define CFZ(call)                                                        \
+    do {                                                                 \
+        cfz_status s_ = (call);                                          \
+        if (s_ != CFZ_OK)                                                \
+            FAIL("%s: %s (%s)", #call, cfz_status_string(s_), cfz_last_error()); \
+    } while (0)
+
+enum { ROWS = 48, COLS = 384, N = ROWS * COLS, STEPS = 4 };  /* COLS: a multiple of every group size used */
+
+static uint32_t lcg(uint32_t *s)
+{
+    *s = *s * 1664525u + 1013904223u;
+    return *s;
+}
+
+/* fp32 -> bf16, round to nearest even (finite inputs) */
+static uint16_t to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+/* STEPS + 1 activations, each a small random walk step from the last */
+static void make_inputs(uint16_t *x, uint32_t seed)
+{
+    float cur[N];
+    for (int j = 0; j < N; ++j)
+        cur[j] = ((float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f) * 4.0f;
+    for (int t = 0; t <= STEPS; ++t) {
+        for (int j = 0; j < N; ++j) {
+            if (t > 0)
+                cur[j] += ((float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f) * 0.25f;
+            x[t * N + j] = to_bf16(cur[j]);
+        }
+    }
+}
+
+static int run_case(int bits, int group, int mode, int state_bf16, const uint16_t *x)
+{
+    printf("case bits=%d group=%d mode=%d state_bf16=%d\n", bits, group, mode, state_bf16);
+    fflush(stdout);
+    const size_t w = state_bf16 ? 2 : 4, nc = (size_t)N * bits / 8, ns = N / group;
+    cfz_desc sd, rd;
+    memset(&sd, 0, sizeof sd);
+    sd.rows = ROWS;
+    sd.cols = COLS;
+    sd.bits = bits;
+    sd.group = group;
+    sd.ef_mode = mode;
+    sd.role = CFZ_SENDER;
+    sd.state_dtype = state_bf16 ? CFZ_STATE_BF16 : CFZ_STATE_F32;
+    rd = sd;
+    rd.ef_mode = CFZ_EF_DELTA;
+    rd.role = CFZ_RECEIVER;
+    if (cfz_codes_bytes(&sd) != nc || cfz_scales_bytes(&sd) != ns * 4)
+        FAIL("payload sizes");
+
+    void *d_x, *d_prev, *d_base, *d_err, *d_codes, *d_scales, *d_rbase, *d_xhat;
+    HIP(hipMalloc(&d_x, 2 * N));
+    HIP(hipMalloc(&d_prev, 2 * N));
+    HIP(hipMalloc(&d_base, w * N));
+    HIP(hipMalloc(&d_err, w * N));
+    HIP(hipMalloc(&d_codes, nc));
+    HIP(hipMalloc(&d_scales, ns * 4));
+    HIP(hipMalloc(&d_rbase, w * N));
+    HIP(hipMalloc(&d_xhat, 2 * N));
+
+    /* host copies: oracle state and what comes back from the device */
+    static uint16_t o_prev[N], o_xhat[N], g_prev[N], g_xhat[N];
+    static uint8_t o_base[4 * N], o_err[4 * N], o_rbase[4 * N], g_base[4 * N], g_err[4 * N],
+        g_rbase[4 * N], o_codes[N], g_codes[N];
+    static float o_scales[N], g_scales[N];
+
+    cfz_buffers sb, rb;
+    sb.prev_bf16 = (uint16_t *)d_prev;
+    sb.base = d_base;
+    sb.err = d_err;
+    rb.prev_bf16 = NULL;
+    rb.base = d_rbase;
+    rb.err = NULL;
+    HIP(hipMemcpy(d_x, x, 2 * N, hipMemcpyHostToDevice));
+    cfz_state *snd = NULL, *rcv = NULL;
+    CFZ(cfz_state_create(&sd, &sb, (const uint16_t *)d_x, NULL, &snd));
+    CFZ(cfz_state_create(&rd, &rb, (const uint16_t *)d_x, NULL, &rcv));
+    oracle_warmup(N, mode, CFZ_SENDER, state_bf16, x, o_prev, o_base, o_err);
+    oracle_warmup(N, CFZ_EF_DELTA, CFZ_RECEIVER, state_bf16, x, NULL, o_rbase, NULL);
+
+    for (int t = 1; t <= STEPS; ++t) {
+        const uint16_t *xt = x + (size_t)t * N;
+        HIP(hipMemcpy(d_x, xt, 2 * N, hipMemcpyHostToDevice));
+        CFZ(cfz_compress(snd, (const uint16_t *)d_x, (uint8_t *)d_codes, (float *)d_scales, NULL));
+        CFZ(cfz_decompress(rcv, (const uint8_t *)d_codes, (const float *)d_scales,
+                           (uint16_t *)d_xhat, NULL));
+        HIP(hipDeviceSynchronize());
+        oracle_compress(N, bits, group, mode, state_bf16, xt, o_prev, o_base, o_err, o_codes,
+                        o_scales);
+        oracle_decompress(N, bits, group, state_bf16, o_codes, o_scales, o_rbase, o_xhat);
+
+        HIP(hipMemcpy(g_codes, d_codes, nc, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(g_scales, d_scales, ns * 4, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(g_rbase, d_rbase, w * N, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(g_xhat, d_xhat, 2 * N, hipMemcpyDeviceToHost));
+        if (memcmp(g_codes, o_codes, nc) || memcmp(g_scales, o_scales, ns * 4))
+            FAIL("step %d: payload differs from the oracle", t);
+        if (memcmp(g_rbase, o_rbase, w * N) || memcmp(g_xhat, o_xhat, 2 * N))
+            FAIL("step %d: receiver base or bf16 output differs from the oracle", t);
+        if (mode == CFZ_EF_DELTA) {
+            HIP(hipMemcpy(g_prev, d_prev, 2 * N, hipMemcpyDeviceToHost));
+            if (memcmp(g_prev, o_prev, 2 * N))
+                FAIL("step %d: prev differs", t);
+        } else {
+            HIP(hipMemcpy(g_base, d_base, w * N, hipMemcpyDeviceToHost));
+            if (memcmp(g_base, o_base, w * N))
+                FAIL("step %d: sender base differs", t);
+        }
+        if (mode != CFZ_EF_OFF) {
+            HIP(hipMemcpy(g_err, d_err, w * N, hipMemcpyDeviceToHost));
+            if (memcmp(g_err, o_err, w * N))
+                FAIL("step %d: carried error differs", t);
+        }
+    }
+    if (cfz_state_steps(snd) != STEPS || cfz_state_steps(rcv) != STEPS)
+        FAIL("step counters");
+    CFZ(cfz_state_destroy(snd));
+    CFZ(cfz_state_destroy(rcv));
+    HIP(hipFree(d_x));
+    HIP(hipFree(d_prev));
+    HIP(hipFree(d_base));
+    HIP(hipFree(d_err));
+    HIP(hipFree(d_codes));
+    HIP(hipFree(d_scales));
+    HIP(hipFree(d_rbase));
+    HIP(hipFree(d_xhat));
+    return 0;
+}
+
+int main(void)
+{
+    static uint16_t x[(STEPS + 1) * N];
+    make_inputs(x, 2024u);
+    if (cfz_abi_version() != CFZ_ABI_VERSION) {
+        fprintf(stderr, "ABI version mismatch\n");
+        return 1;
+    }
+    const int cases[][4] = {
+        {4, 64, CFZ_EF_DELTA, 0}, {2, 32, CFZ_EF_DELTA, 0}, {4, 64, CFZ_EF_DELTA, 1},
+        {4, 32, CFZ_EF_LITERAL, 0}, {2, 64, CFZ_EF_OFF, 0}, {4, 128, CFZ_EF_OFF, 1},
+    };
+    for (size_t i = 0; i < sizeof cases / sizeof cases[0]; ++i)
+        if (run_case(cases[i][0], cases[i][1], cases[i][2], cases[i][3], x))
+            return 1;
+    printf("OK\n");
+    return 0;
+}
