@@ -3,10 +3,12 @@
  * memory from the HIP runtime API, every call through the C ABI of libcfz.so,
  * no Python and no torch.  Each step's codes, scales, sender state, receiver
  * base and bf16 output are copied back and compared byte for byte with the CPU
- * oracle (oracle/libcfz_oracle.so, test infrastructure) run on the same inputs.
- * Prints one line per case before its GPU work, and "OK" at the end.
+ * oracle (oracle/libcfz_oracle.so, test infrastructure) run on the same inputs;
+ * cfz_lowrank's reconstruction is compared with the oracle's fp64 one.  Prints
+ * one line per case before its GPU work, and "OK" at the end.
  */
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -21,6 +23,8 @@ void oracle_compress(int64_t n, int bits, int group, int mode, int state_bf16, c
                      uint16_t *prev, void *base, void *err, uint8_t *codes, float *scales);
 void oracle_decompress(int64_t n, int bits, int group, int state_bf16, const uint8_t *codes,
                        const float *scales, void *base, uint16_t *xhat);
+void oracle_lowrank(int64_t m, int64_t n, int r, int T, const uint16_t *A_bf16, const float *Q0,
+                    double *U, double *V, double *RU);
 
 #define FAIL(...)                                                        \
     do {                                                                 \
@@ -172,6 +176,102 @@ static int run_case(int bits, int group, int mode, int state_bf16, const uint16_
     return 0;
 }
 
+/* (U R_U) V^T of one matrix, fp64, from fp32 or fp64 factors */
+static void reconstruct(int m, int n, int r, const double *U, const double *V, const double *RU,
+                        double *D)
+{
+    for (int i = 0; i < m; ++i)
+        for (int j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < r; ++k) {
+                double ur = 0.0;
+                for (int l = 0; l < r; ++l)
+                    ur += U[i * r + l] * RU[l * r + k];
+                acc += ur * V[j * r + k];
+            }
+            D[i * n + j] = acc;
+        }
+}
+
+/* cfz_lowrank on a batch of rank-r + noise matrices (r = 8, so the subspace is well defined): the reconstruction U R_U V^T of every
+ * matrix within 1e-3 (relative Frobenius) of the oracle's fp64 one */
+static int run_lowrank(void)
+{
+    enum { B = 3, M = 64, NN = 128, R = 8, T = 2 };
+    printf("case lowrank batch=%d m=%d n=%d r=%d T=%d\n", B, M, NN, R, T);
+    fflush(stdout);
+    static uint16_t A[B * M * NN];
+    static float Q0[B * NN * R], U[B * M * R], V[B * NN * R], RU[B * R * R];
+    static double Uo[M * R], Vo[NN * R], RUo[R * R], Ug[M * R], Vg[NN * R], RUg[R * R];
+    static double Do[M * NN], Dg[M * NN];
+    uint32_t seed = 77u;
+    for (int b = 0; b < B; ++b) {
+        float f[M * R], g[NN * R];
+        for (int i = 0; i < M * R; ++i)
+            f[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+        for (int i = 0; i < NN * R; ++i)
+            g[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+        for (int i = 0; i < M; ++i)
+            for (int j = 0; j < NN; ++j) {
+                float a = 0.01f * ((float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f);
+                for (int k = 0; k < R; ++k)
+                    a += f[i * R + k] * g[j * R + k];
+                A[(b * M + i) * NN + j] = to_bf16(a);
+            }
+    }
+    for (int i = 0; i < B * NN * R; ++i)
+        Q0[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+
+    const size_t ws_bytes = cfz_lowrank_workspace_bytes(B, M, NN, R);
+    if (ws_bytes == 0)
+        FAIL("workspace size");
+    void *dA, *dQ0, *dU, *dV, *dRU, *dws;
+    HIP(hipMalloc(&dA, sizeof A));
+    HIP(hipMalloc(&dQ0, sizeof Q0));
+    HIP(hipMalloc(&dU, sizeof U));
+    HIP(hipMalloc(&dV, sizeof V));
+    HIP(hipMalloc(&dRU, sizeof RU));
+    HIP(hipMalloc(&dws, ws_bytes));
+    HIP(hipMemcpy(dA, A, sizeof A, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(dQ0, Q0, sizeof Q0, hipMemcpyHostToDevice));
+    if (cfz_lowrank(B, M, NN, R, T, (const uint16_t *)dA, (const float *)dQ0, (float *)dU,
+                    (float *)dV, (float *)dRU, dws, ws_bytes - 1, NULL) != CFZ_ERR_WORKSPACE)
+        FAIL("a short workspace must be refused");
+    CFZ(cfz_lowrank(B, M, NN, R, T, (const uint16_t *)dA, (const float *)dQ0, (float *)dU,
+                    (float *)dV, (float *)dRU, dws, ws_bytes, NULL));
+    HIP(hipDeviceSynchronize());
+    HIP(hipMemcpy(U, dU, sizeof U, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(V, dV, sizeof V, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(RU, dRU, sizeof RU, hipMemcpyDeviceToHost));
+    for (int b = 0; b < B; ++b) {
+        oracle_lowrank(M, NN, R, T, A + (size_t)b * M * NN, Q0 + (size_t)b * NN * R, Uo, Vo, RUo);
+        for (int i = 0; i < M * R; ++i)
+            Ug[i] = U[b * M * R + i];
+        for (int i = 0; i < NN * R; ++i)
+            Vg[i] = V[b * NN * R + i];
+        for (int i = 0; i < R * R; ++i)
+            RUg[i] = RU[b * R * R + i];
+        reconstruct(M, NN, R, Uo, Vo, RUo, Do);
+        reconstruct(M, NN, R, Ug, Vg, RUg, Dg);
+        double num = 0.0, den = 0.0;
+        for (int i = 0; i < M * NN; ++i) {
+            num += (Dg[i] - Do[i]) * (Dg[i] - Do[i]);
+            den += Do[i] * Do[i];
+        }
+        const double rel = sqrt(num / den);
+        printf("  matrix %d: reconstruction within %.2e of the oracle\n", b, rel);
+        if (!(rel <= 1e-3))
+            FAIL("matrix %d: reconstruction differs from the oracle by %.3e", b, rel);
+    }
+    HIP(hipFree(dA));
+    HIP(hipFree(dQ0));
+    HIP(hipFree(dU));
+    HIP(hipFree(dV));
+    HIP(hipFree(dRU));
+    HIP(hipFree(dws));
+    return 0;
+}
+
 int main(void)
 {
     static uint16_t x[(STEPS + 1) * N];
@@ -187,6 +287,8 @@ int main(void)
     for (size_t i = 0; i < sizeof cases / sizeof cases[0]; ++i)
         if (run_case(cases[i][0], cases[i][1], cases[i][2], cases[i][3], x))
             return 1;
+    if (run_lowrank())
+        return 1;
     printf("OK\n");
     return 0;
 }

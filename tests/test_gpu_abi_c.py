@@ -2,7 +2,8 @@
 device memory with the HIP runtime API, calls libcfz only through include/cfz.h
 (no Python, no torch) and compares every step's codes, scales, states and bf16
 output byte for byte with the C oracle, over int4/int2, group sizes 32-128, the
-three error-feedback modes and fp32/bf16 state."""
+three error-feedback modes and fp32/bf16 state; then cfz_lowrank from C, its
+reconstruction within 1e-3 of the oracle's."""
 import os
 import shutil
 import subprocess
@@ -33,7 +34,7 @@ def test_c_client_runs_the_codec_bit_exact(tmp_path):
                         "-I", os.path.join(ROCM, "include"), "-I", INC,
                         os.path.join(ROOT, "tests", "abi_c", "gpu_client.c"),
                         "-L", LIBDIR, "-lcfz", "-L", ORACLE_DIR, "-l:libcfz_oracle.so",
-                        "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + rpath,
+                        "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm", "-Wl,-rpath," + rpath,
                         "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     print("[gpu] C client", file=sys.stderr, flush=True)
