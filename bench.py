@@ -165,42 +165,61 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
     return out
 
 
-def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps=6, pool=4):
+def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps=6):
     """The rank-r compressor inside error feedback on 57 layers of 1024 x 3072 per step:
     activations drift by rank 16 + noise per step.  One step = one sender call (residual,
-    subspace iteration, error update) and one receiver call (base update + bf16 output)."""
+    subspace iteration, error update) and one receiver call (base update + bf16 output).
+    Timed with a fresh random Q0 per step; then, over the same consecutive steps, the
+    receiver's relative error ||base - x|| / ||x|| with random or warm-started Q0 (the
+    previous step's V) at T = 1 and T = 2."""
     from synth import LowrankDrift, gaussian_q0
 
     st = LowrankDrift(batch, m, n, rank=16, seed=3, device=dev)
-    X = [st.next() for _ in range(pool + 1)]
+    X = [st.next() for _ in range(steps + 2)]  # consecutive steps: warm-up + steps + 1
     del st
-    Q0 = [gaussian_q0(batch, n, r, seed=s, device=dev) for s in range(pool)]
-    snd = cfz.LowrankSender(batch, m, n, r, x0=X[0])
-    rcv = cfz.LowrankReceiver(batch, m, n, r, x0=X[0])
+    Q0 = [gaussian_q0(batch, n, r, seed=s, device=dev) for s in range(steps + 1)]
     xhat = torch.empty(batch * m * n, dtype=torch.bfloat16, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
-    for k in range(steps + 1):  # the first step is an untimed warm-up
-        ev[k][0].record()
-        snd.compress(X[1 + k % pool], Q0[k % pool], T)
-        ev[k][1].record()
-        rcv.decompress(snd.U, snd.V, snd.RU, xhat)
-        ev[k][2].record()
-    torch.cuda.synchronize()
-    tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / steps
-    td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / steps
+
+    def run(T_, warm, timed):
+        snd = cfz.LowrankSender(batch, m, n, r, x0=X[0])
+        rcv = cfz.LowrankReceiver(batch, m, n, r, x0=X[0])
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
+        for k in range(steps + 1):  # the first step is an untimed warm-up
+            q = snd.V.clone() if (warm and k > 0) else Q0[k]
+            ev[k][0].record()
+            snd.compress(X[1 + k], q, T_)
+            ev[k][1].record()
+            rcv.decompress(snd.U, snd.V, snd.RU, xhat)
+            ev[k][2].record()
+        torch.cuda.synchronize()
+        tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / steps
+        td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / steps
+        x_last = X[steps + 1].float().reshape(-1)
+        rel = (torch.linalg.vector_norm(rcv.base - x_last) / torch.linalg.vector_norm(x_last)).item()
+        del snd, rcv
+        return tc, td, rel
+
+    tc, td, rel = run(T, False, True)
+    accuracy = {}
+    for T_, warm in ((1, False), (2, False), (1, True), (2, True)):
+        c, _, e = run(T_, warm, False)
+        accuracy[f"{'warm' if warm else 'random'}_Q0_T{T_}"] = {
+            "compress_ms": round(c * 1e3, 4), "receiver_rel_error_last_step": float(f"{e:.4g}")}
     elems = batch * m * n
     payload = batch * 4 * (m * r + r * r + n * r)
     upd_bytes = 10 * elems  # read + write fp32 base, write bf16 xhat
-    del snd, rcv, X, Q0, xhat
+    del X, Q0, xhat
     return {"workload": f"{batch} x {m}x{n}, activations drifting by rank 16 + 0.05 noise, "
                         f"r={r}, T={T}, random Q0 each step", "steps": steps,
             "activation_GB/s": round(2 * elems / (tc + td) / 1e9, 2),
             "compress_ms": round(tc * 1e3, 4), "decompress_ms": round(td * 1e3, 4),
+            "receiver_rel_error_last_step": float(f"{rel:.4g}"),
             "compression_ratio_vs_bf16": round(2 * elems / payload, 1),
             "decompress_update_kernel": {
                 "GB/s": round(upd_bytes / td / 1e9, 1),
                 "frac_hbm_peak": round(upd_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
-                "bytes_per_elem": 10}}
+                "bytes_per_elem": 10},
+            "q0_and_T": accuracy}
 
 
 def bench_ef_modes(cfz, torch, X, slots, rows, cols, steps=10):
