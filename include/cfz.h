@@ -176,7 +176,9 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
  * matrix and r x r Cholesky in fp64); a column whose pivot is <= 1e-13 of the
  * mean squared column norm is dropped (zero column of Q, zero row and column
  * of R).  The reconstruction of A is U R_U V^T = (A Q) Q^T.
- * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn).
+ * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn); it
+ * may be the V buffer itself (a warm start from the previous call's V): Q0 is
+ * read in full before V is written.
  * U: [batch][m][r], V: [batch][n][r], RU: [batch][r][r], fp32 outputs.
  * Requires 1 <= r <= 32, r <= m, r <= n, T >= 0, n a multiple of 8 (rows of A
  * are 16-byte aligned), m, n, batch <= 2^20, m * n <= 2^30, batch >= 0 (0 is a no-op); a
@@ -221,7 +223,8 @@ cfz_status cfz_lowrank_ef_warmup(int64_t count, const uint16_t *x0_bf16, uint16_
                                  float *err, float *base, void *hip_stream);
 
 /* One sender step (above).  Q0: [batch][n][r] fp32 random sample of the
- * subspace iteration; passing the previous step's V warm-starts it.  Outputs
+ * subspace iteration; passing the previous step's V warm-starts it (Q0 may be
+ * the V buffer itself: it is read in full before V is written).  Outputs
  * U, V, RU; updates prev and err in place.  Workspace: at least
  * cfz_lowrank_ef_workspace_bytes(batch, m, n, r) bytes, 256-byte aligned.
  * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_WORKSPACE,

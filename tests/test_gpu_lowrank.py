@@ -155,3 +155,23 @@ def test_full_size_layer_batch(r):
         Q0 = gaussian_q0(batch, n, r, seed=2000 + step, device=DEV).cpu()
         check(A, Q0, r, T, layers=[0, 56], lead=16 if r == 32 else None,
               tag=f"full r={r} step={step}")
+
+
+@pytest.mark.parametrize("T", [0, 2])
+def test_q0_may_be_the_v_buffer(T):
+    """Warm start in place: passing the previous call's V as Q0 (the same buffer) gives the bits
+    of passing a copy of it -- Q0 is read in full before V is written."""
+    batch, m, n, r = 2, 128, 192, 8
+    say(f"[gpu] low-rank Q0 aliasing V, T={T}")
+    A = lowrank_batch(batch, m, n, seed=31).to(DEV)
+    ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(batch, m, n, r), dtype=torch.uint8,
+                     device=DEV)
+    U, V, RU = (torch.empty(batch, m, r, device=DEV), torch.empty(batch, n, r, device=DEV),
+                torch.empty(batch, r, r, device=DEV))
+    cfz.cfz_lowrank(batch, m, n, r, 2, A, gaussian_q0(batch, n, r, seed=3).to(DEV), U, V, RU, ws)
+    q_copy = V.clone()
+    U2, V2, RU2 = torch.empty_like(U), torch.empty_like(V), torch.empty_like(RU)
+    cfz.cfz_lowrank(batch, m, n, r, T, A, q_copy, U2, V2, RU2, ws)
+    cfz.cfz_lowrank(batch, m, n, r, T, A, V, U, V, RU, ws)  # Q0 and V: one buffer
+    torch.cuda.synchronize()
+    assert torch.equal(U, U2) and torch.equal(V, V2) and torch.equal(RU, RU2)
