@@ -28,6 +28,11 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def raw_bytes(t):
+    """The bytes of a device tensor (any element type, bf16 included) as a numpy uint8 array."""
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
 def u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
 
@@ -502,3 +507,56 @@ def test_lost_payload_then_rewarm_in_place():
         _compare_step(f"re-warmed step {t}", gs, gr, c1, s1, os_, or_, oc, osc)
     for h in (gs, gr, fs, fr):
         h.close()
+
+
+@pytest.mark.parametrize("bits,group,sb", [(4, 64, False), (2, 32, True)])
+def test_beyond_2_pow_31_elements_sampled_groups(bits, group, sb):
+    """One tensor of 524,544 x 4096 = 2,148,532,224 elements (past 2^31: 64-bit indexing of
+    elements, quads, codes and scales), one warm-up and one compressed step at the sender and
+    the receiver; 24 groups spread over the tensor -- including those around element 2^31 and
+    the last one -- compared bit for bit with the oracle run on those groups alone."""
+    rows, cols = 524544, 4096
+    n = rows * cols
+    assert n > 2 ** 31
+    say(f"[gpu] beyond 2^31 elements: {rows} x {cols}, int{bits} g{group}, bf16 state={sb}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    x0 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    x1 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    chunk = 1 << 28
+    for o in range(0, n, chunk):  # fp32 draws a chunk at a time, kept as bf16
+        k = min(chunk, n - o)
+        a = torch.randn(k, generator=g, device=DEV)
+        x0[o:o + k] = a.bfloat16()
+        x1[o:o + k] = (0.98 * a + 0.2 * torch.randn(k, generator=g, device=DEV)).bfloat16()
+        del a
+    snd = cfz.Sender(rows, cols, bits, group, x0=x0, state_bf16=sb)
+    rcv = cfz.Receiver(rows, cols, bits, group, x0=x0, state_bf16=sb)
+    xhat = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    snd.compress(x1)
+    rcv.decompress(snd.codes, snd.scales, xhat)
+    torch.cuda.synchronize()
+    ngroups = n // group
+    edge = 2 ** 31 // group
+    picks = sorted({0, 1, ngroups // 3, ngroups // 2, edge - 2, edge - 1, edge, edge + 1,
+                    ngroups - 2, ngroups - 1} |
+                   {int(v) for v in np.linspace(2, ngroups - 3, 14)})
+    per_code = group * bits // 8
+    for gi in picks:
+        lo, hi = gi * group, (gi + 1) * group
+        os_ = oracle.Sender(group, bits, group, oracle.DELTA, x0=u16(x0[lo:hi]), state_bf16=sb)
+        or_ = oracle.Receiver(group, bits, group, x0=u16(x0[lo:hi]), state_bf16=sb)
+        oc, osc = os_.compress(u16(x1[lo:hi]))
+        oxh = or_.decompress(oc, osc, want_xhat=True)
+        tag = f"group {gi} (elements {lo}..{hi - 1})"
+        assert np.array_equal(snd.codes[gi * per_code:(gi + 1) * per_code].cpu().numpy(), oc), \
+            f"{tag}: codes"
+        assert snd.scales[gi:gi + 1].cpu().numpy().view(np.uint32)[0] == \
+            osc.view(np.uint32)[0], f"{tag}: scale"
+        assert np.array_equal(u16(snd.prev[lo:hi]), os_.prev), f"{tag}: prev"
+        assert np.array_equal(raw_bytes(snd.err[lo:hi]), os_.err.view(np.uint8)), f"{tag}: err"
+        assert np.array_equal(raw_bytes(rcv.base[lo:hi]), or_.base.view(np.uint8)), \
+            f"{tag}: receiver base"
+        assert np.array_equal(u16(xhat[lo:hi]), oxh[1] if isinstance(oxh, tuple) else oxh), \
+            f"{tag}: xhat"
+    say(f"  {len(picks)} groups bit-exact, including groups {edge - 1} and {edge} at 2^31")
