@@ -175,3 +175,34 @@ def test_q0_may_be_the_v_buffer(T):
     cfz.cfz_lowrank(batch, m, n, r, T, A, V, U, V, RU, ws)  # Q0 and V: one buffer
     torch.cuda.synchronize()
     assert torch.equal(U, U2) and torch.equal(V, V2) and torch.equal(RU, RU2)
+
+
+def test_largest_matrix_exact_rank():
+    """The largest matrix the call takes, m * n = 2^30 (16384 x 65536 bf16, 2 GiB; its byte
+    offsets span the whole 32-bit buffer range): an exactly rank-8 input (ternary factors, so
+    every entry is an exact bf16 integer) is reproduced by U R_U V^T on 64 sampled rows,
+    and U, V have orthonormal columns -- properties that hold at any size, checked in fp64."""
+    m, n, r = 16384, 65536, 8
+    say(f"[gpu] low-rank largest matrix {m} x {n}, r={r}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    f = torch.randint(-1, 2, (m, r), generator=g, device=DEV).float()
+    gg = torch.randint(-1, 2, (n, r), generator=g, device=DEV).float()
+    A = (f @ gg.T.contiguous()).bfloat16()  # integers of size <= 8: exact in fp32 and bf16
+    assert A.numel() == 2 ** 30
+    Q0 = gaussian_q0(1, n, r, seed=4).to(DEV)
+    U, V, RU = (torch.empty(1, m, r, device=DEV), torch.empty(1, n, r, device=DEV),
+                torch.empty(1, r, r, device=DEV))
+    ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(1, m, n, r), dtype=torch.uint8, device=DEV)
+    cfz.cfz_lowrank(1, m, n, r, 1, A, Q0, U, V, RU, ws)
+    torch.cuda.synchronize()
+    Ud, Vd, Rd = U[0].double(), V[0].double(), RU[0].double()
+    eye = torch.eye(r, dtype=torch.float64, device=DEV)
+    assert (Ud.T @ Ud - eye).abs().max().item() < 1e-5
+    assert (Vd.T @ Vd - eye).abs().max().item() < 1e-5
+    rows = torch.tensor(sorted({0, 1, m // 2, m - 2, m - 1} |
+                               {int(v) for v in np.linspace(2, m - 3, 59)}), device=DEV)
+    D = (Ud[rows] @ Rd) @ Vd.T
+    err = (D - A[rows].double()).abs().max().item()
+    say(f"  sampled rows reproduced to {err:.2e} (entries up to 8)")
+    assert err < 1e-4 * 8
