@@ -310,3 +310,40 @@ def test_binding_rejects_wrong_element_types():
         cfz.cfz_lowrank(1, 64, 128, 8, 1, torch.empty(64 * 128, dtype=torch.bfloat16),
                         torch.empty(128 * 8, dtype=torch.float16), torch.empty(64 * 8),
                         torch.empty(128 * 8), torch.empty(64), torch.empty(16, dtype=torch.uint8))
+
+
+def test_last_error_is_per_thread():
+    """cfz_last_error() describes the calling thread's last failure: two threads failing in
+    different ways at the same time each read their own message."""
+    import threading
+    lib = cfz._lib
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, call):
+        for _ in range(200):
+            barrier.wait()
+            st = call()
+            barrier.wait()
+            seen.setdefault(name, set()).add((st, lib.cfz_last_error().decode()))
+
+    def bad_bits():
+        d = cfz.make_desc(4, 64, bits=3)
+        return lib.cfz_state_resume(C.byref(d), C.byref(cfz.cfz_buffers(ALIGNED, None, ALIGNED)),
+                                    0, C.byref(C.c_void_p()))
+
+    def bad_rank():
+        return lib.cfz_lowrank(1, 64, 64, 40, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                               ALIGNED, 1 << 20, None)
+
+    ts = [threading.Thread(target=worker, args=("bits", bad_bits)),
+          threading.Thread(target=worker, args=("rank", bad_rank))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert len(seen["bits"]) == 1 and len(seen["rank"]) == 1
+    (sb, mb), = seen["bits"]
+    (sr, mr), = seen["rank"]
+    assert sb == cfz.CFZ_ERR_UNSUPPORTED and "bits" in mb
+    assert sr == cfz.CFZ_ERR_SHAPE and "rank" in mr
