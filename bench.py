@@ -1,17 +1,24 @@
 """Throughput of the residual codec on one MI355X.
 
-One step = one denoising step of the FLUX.1-dev share at patch degree 4: for
-each of the 57 layers' K and V (114 tensors of 1024 tokens x 3072 channels,
-bf16), one fused compress launch (residual + error feedback + int4 group-64
-quantization + state update, DELTA mode) and one decode launch (unpack + base
-update).  Inputs are seeded AR(1) activations, generated into HBM before the
-timed region; the per-tensor launches of one step are captured once into HIP
-graphs and replayed.
+One step = one denoising step of the FLUX.1-dev share at patch degree 4: the
+57 layers' K and V (114 tensors of 1024 tokens x 3072 channels, bf16), each
+layer's pair in one grouped compress launch (residual + error feedback + int4
+group-64 quantization + state update, DELTA mode) and one grouped decode launch
+(unpack + base update).  Inputs are seeded AR(1) activations, generated into
+HBM before the timed region; the launches of one step are captured once into
+HIP graphs and replayed.
 
 value = bf16 activation bytes coded per second: 2 bytes x elements per step x
 steps / elapsed (compress + decode).  The roofline entry is for the compress
 kernel: algorithmic bytes per launch over its average launch duration, timed
 with HIP events on the stream the kernels run on.
+
+Further legs in the same JSON line: other launch granularities (per tensor,
+16 tensors), the three error-feedback readings with their receiver error,
+bf16 state, int2 group-32 over all tensors in one launch, the CogVideoX-2b
+share, the subspace iteration at r = 8/16/32, the rank-r compressor inside
+error feedback (random or warm-started Q0), and the CPU oracle on a bounded
+sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 27] [--warmup 1] [--no-cpu-baseline]
 """
