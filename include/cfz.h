@@ -135,6 +135,10 @@ size_t cfz_scales_bytes(const cfz_desc *desc);
  * x: rows*cols bf16.  codes: cfz_codes_bytes.  scales: rows*cols/group fp32,
  * scale k covering elements [k*group, (k+1)*group).
  * (paper: abstract -- compressed step-wise residuals with error feedback.)
+ * NaN and +-Inf in x lie outside the method: the call still writes only its own
+ * buffers, and only the groups that hold such values get unspecified codes,
+ * scales and state (their error and base elements can stay non-finite until the
+ * state is warmed again with cfz_state_create); every other group is unaffected.
  * Errors: CFZ_ERR_NULL, CFZ_ERR_ALIGN, CFZ_ERR_MODE (receiver state), CFZ_ERR_HIP. */
 cfz_status cfz_compress(cfz_state *sender, const uint16_t *x_bf16, uint8_t *codes,
                         float *scales, void *hip_stream);

@@ -162,6 +162,60 @@ def test_extreme_magnitudes(state_bf16):
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("bits,group,sb", [(4, 64, False), (2, 32, True)])
+def test_non_finite_values_stay_in_their_group(bits, group, mode, sb):
+    """NaN and +-Inf activations lie outside the method's domain; what the library promises
+    is that they touch only the groups that hold them.  A NaN, a +Inf and a -Inf go into three
+    groups of step 1 (the oracle gets the clean values there); over that step and two clean
+    steps after it, every other group's codes, scales, error, previous activation, bases and
+    reconstruction equal the oracle's bits -- the residual, the scale, the codes and the state
+    updates never mix groups."""
+    rows, cols = 64, 512
+    n = rows * cols
+    xs = [x[0] for x in _ar1(rows, cols, 4, seed=41 + mode)]
+    spots = [(3, 7, float("nan")), (20, 300, float("inf")), (63, 511, float("-inf"))]
+    bad = np.zeros(n // group, bool)
+    dirty = xs[1].clone()
+    for r, c, v in spots:
+        dirty[r, c] = v
+        bad[(r * cols + c) // group] = True
+    ok_elem = np.repeat(~bad, group)
+    ok_byte = np.repeat(~bad, group * bits // 8)
+    say(f"[gpu] non-finite inputs b{bits} g{group} m{mode} bf16 state={sb}")
+    gs = cfz.Sender(rows, cols, bits, group, mode, x0=xs[0].to(DEV), state_bf16=sb)
+    gr = cfz.Receiver(rows, cols, bits, group, x0=xs[0].to(DEV), state_bf16=sb)
+    os_ = oracle.Sender(n, bits, group, MODE_PAIRS[mode], x0=u16(xs[0]), state_bf16=sb)
+    or_ = oracle.Receiver(n, bits, group, x0=u16(xs[0]), state_bf16=sb)
+    xhat = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    for t in (1, 2, 3):
+        codes, scales = gs.compress((dirty if t == 1 else xs[t]).to(DEV))
+        gr.decompress(codes, scales, xhat)
+        oc, osc = os_.compress(u16(xs[t]))
+        ox = or_.decompress(oc, osc, want_xhat=True)
+        torch.cuda.synchronize()
+        tag = f"step {t}"
+        sc = scales.cpu().numpy()
+        if t == 1:  # the injected values reached the kernel: |+-Inf| makes its group's scale Inf
+            for r, c, v in spots[1:]:
+                assert np.isinf(sc[(r * cols + c) // group]), tag
+        assert np.array_equal(codes.cpu().numpy()[ok_byte], oc[ok_byte]), f"{tag}: codes"
+        assert np.array_equal(sc.view(np.uint32)[~bad], osc.view(np.uint32)[~bad]), \
+            f"{tag}: scales"
+        if os_.err is not None:
+            assert np.array_equal(sbits(gs.err)[ok_elem], obits(os_.err)[ok_elem]), f"{tag}: err"
+        if os_.prev is not None:
+            assert np.array_equal(u16(gs.prev)[ok_elem], os_.prev[ok_elem]), f"{tag}: prev"
+        if os_.base is not None:
+            assert np.array_equal(sbits(gs.base)[ok_elem], obits(os_.base)[ok_elem]), \
+                f"{tag}: sender base"
+        assert np.array_equal(sbits(gr.base)[ok_elem], obits(or_.base)[ok_elem]), \
+            f"{tag}: receiver base"
+        assert np.array_equal(u16(xhat)[ok_elem], ox[ok_elem]), f"{tag}: xhat"
+    gs.close()
+    gr.close()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("group", [8, 32, 128])
 @pytest.mark.parametrize("bits", [4, 2])
 def test_bf16_state_several_tiles_and_ragged_tail(bits, group, mode):
