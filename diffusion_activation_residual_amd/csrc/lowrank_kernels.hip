@@ -39,6 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kGramRows = 256;    // rows of M per Gram work-group (64 per wave)
 constexpr int kApplyRows = 256;   // rows of M per apply work-group (64 per wave)
 constexpr int kCholThreads = 64;  // the r x r factorisation runs on one wavefront
+constexpr int kMaxPartials = 8;   // partial sums of Z the Gram kernel adds up
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -62,13 +63,23 @@ struct Layout {
     int rp;
     int64_t mp, np;             // m, n padded to 64
     int64_t gram_blocks;        // max over (m, n) of row blocks of the Gram kernel
+    int splits;                 // row ranges of the one-pass A^T (A Q); 0: two passes
+    int64_t split_rows;         // rows per range, a multiple of the 16-row panel
     size_t off_qops, off_yops, off_mf, off_gram, off_r1, off_r1inv, off_rinv;
     size_t layer_bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout make_layout(int64_t m, int64_t n, int r)
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+// Row ranges per matrix for the one-pass A^T (A Q) (declared with its kernel
+// below): about one 1024-thread work-group per compute unit over the batch, at
+// most kAtaMaxSplits partial sums per matrix.  0 where the pass does not apply
+// (r > 16 or n > 3072): then A Q and A^T Y run as two passes.
+int ata_splits(int64_t batch, int64_t m, int64_t n, int r);
+
+Layout make_layout(int64_t batch, int64_t m, int64_t n, int r)
 {
     Layout L;
     L.rp = r <= 16 ? 16 : 32;
@@ -76,10 +87,14 @@ Layout make_layout(int64_t m, int64_t n, int r)
     L.np = round_up(n, 64);
     const int64_t lmax = m > n ? m : n;
     L.gram_blocks = (lmax + kGramRows - 1) / kGramRows;
+    L.splits = ata_splits(batch, m, n, r);
+    L.split_rows = L.splits ? round_up((m + L.splits - 1) / L.splits, 16) : 0;
+    // Z or P in fp32 [L][r]; with the one-pass product, Z's partial sums side by side
+    const int64_t mf_rows = L.splits * n > lmax ? L.splits * n : lmax;
     size_t off = 0;
     L.off_qops = off; off = align256(off + (size_t)L.np * L.rp * 2 * 2);
     L.off_yops = off; off = align256(off + (size_t)L.mp * L.rp * 2 * 2);
-    L.off_mf = off;   off = align256(off + (size_t)lmax * r * 4);
+    L.off_mf = off;   off = align256(off + (size_t)mf_rows * r * 4);
     L.off_gram = off; off = align256(off + (size_t)L.gram_blocks * L.rp * L.rp * 8);
     L.off_r1 = off;   off = align256(off + (size_t)L.rp * L.rp * 8);
     L.off_r1inv = off; off = align256(off + (size_t)L.rp * L.rp * 8);
@@ -420,6 +435,201 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     }
 }
 
+// ------------------------------------------------------------------ Z = A^T (A Q), one pass
+
+// Step 3 of the iteration with each row panel of A read from HBM once.  A
+// work-group owns a contiguous range of rows of one matrix (one of `splits`
+// ranges) and walks it in 8-row panels; a panel (8 full rows, contiguous in
+// memory) goes through LDS, where
+//   phase 1: each wave multiplies the panel's columns of its own 32-column
+//            blocks by Q (hi + lo) into a partial Y (8 rows in a 16-row MFMA
+//            tile), and the 16 partials are summed in wave order and split
+//            into bf16 hi + lo;
+//   phase 2: each wave adds panel^T Y to its blocks' rows of Z, read back with
+//            the transposing LDS load; hi and lo ride in one K = 16 MFMA
+//            (k = 0..7 the panel's rows against Y hi, 8..15 against Y lo).
+// Each wave holds its blocks' Q hi (24 registers; Q lo sits in wave-private
+// LDS slots) and its rows of Z (48) for the whole kernel, so the only memory
+// loads in the loop are the panels: every wave keeps its share of the next
+// panel (3 x 16 bytes per lane) in flight from the moment the current one is
+// in LDS.  Vector loads return
+// in issue order, so any other load issued behind a panel would wait for it.
+// Z is written once per work-group as one fp32 [n][r] partial; the Gram kernel
+// sums the `splits` partials in a fixed order.  RP = 16 only.
+constexpr int kAtaWaves = 16;
+constexpr int kAtaThreads = 64 * kAtaWaves;
+constexpr int kAtaPanel = 8;                           // rows per panel
+constexpr int kAtaMaxBlocks = 6;                       // 32-column blocks per wave
+constexpr int64_t kAtaMaxN = (int64_t)kAtaWaves * kAtaMaxBlocks * 32;  // 3072
+constexpr int kAtaChunks = (int)(kAtaMaxN / 8 / 128);  // 16-byte loads per lane: half a row per wave
+constexpr int kAtaMaxSplits = 8;
+// LDS row stride: the row padded to 128 columns plus 24, so that consecutive rows
+// start 12 banks apart -- the rows of a phase 1 read and the 4 rows of a
+// transposing read then touch distinct banks.
+constexpr int kAtaSrowMax = (int)kAtaMaxN + 24;
+static_assert(kAtaWaves == 2 * kAtaPanel && kAtaMaxN == 2 * 8 * 64 * kAtaChunks,
+              "two waves load each panel row, kAtaChunks 16-byte loads per lane each");
+
+typedef short i16x4k __attribute__((ext_vector_type(4)));
+
+template <int RP>
+__global__ void __launch_bounds__(kAtaThreads)
+lr_ata_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
+              size_t layer_bytes, size_t off_qops, size_t off_z, int64_t np, int splits,
+              int64_t split_rows)
+{
+    static_assert(RP == 16, "the one-pass product keeps Z in registers only for RP = 16");
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / splits, s = lid % splits;
+    uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    const bf16x8 *qhi = (const bf16x8 *)(wsb + off_qops);
+    const bf16x8 *qlo = qhi + (np / 8) * RP;
+    float *zpart = (float *)(wsb + off_z) + (size_t)s * n * r;
+
+    const int64_t row0 = (int64_t)s * split_rows;
+    const int64_t rows_here = m - row0 <= 0 ? 0 : (m - row0 < split_rows ? m - row0 : split_rows);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (int64_t)b * m * n + row0 * n, (uint32_t)(rows_here * n * 2));
+
+    __shared__ __attribute__((aligned(16))) uint16_t sp[kAtaPanel * kAtaSrowMax];
+    __shared__ float sy[kAtaWaves][kAtaPanel * 16];
+    __shared__ i16x4k syo[2][2][16];  // [hi, lo][rows 0..3, 4..7][column of Y]
+    __shared__ bf16x8 sql[kAtaWaves][kAtaMaxBlocks][64];  // each wave's Q lo operands
+
+    // the wave index in a scalar register, so that every per-wave offset below is too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
+    const int nb = (int)((n + 31) / 32);                   // 32-column blocks
+    const int nbw = (nb + kAtaWaves - 1) / kAtaWaves;      // blocks per wave (<= kAtaMaxBlocks)
+    const int kb0 = wave * nbw;
+    const int kbn = nb - kb0 < nbw ? nb - kb0 : nbw;       // this wave's blocks (may be <= 0)
+    const int srow = (int)round_up(32 * nb, 128) + 24;
+    const int cpr = (int)(n / 8);                          // 16-byte chunks per row
+    const int prow = wave >> 1;                            // the panel row this wave loads
+    const int chalf = (wave & 1) * (64 * kAtaChunks);      // and its first chunk
+
+    auto load_panel = [&](int64_t p, u32x4 (&v)[kAtaChunks]) {
+        const uint32_t base = (uint32_t)((p * kAtaPanel + prow) * n * 2);
+#pragma unroll
+        for (int k = 0; k < kAtaChunks; ++k) {
+            const int cc = chalf + lane + 64 * k;
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, cc < cpr ? base + (uint32_t)cc * 16 : kOOB, 0, 2 /*nt*/);
+        }
+    };
+    auto store_panel = [&](const u32x4 (&v)[kAtaChunks]) {
+#pragma unroll
+        for (int k = 0; k < kAtaChunks; ++k) {
+            const int cc = chalf + lane + 64 * k;
+            if (cc < cpr)
+                *(u32x4 *)&sp[prow * srow + 8 * cc] = v[k];
+        }
+    };
+
+    u32x4 pf[kAtaChunks];
+    load_panel(0, pf);
+
+    // Q operands of this wave's blocks: slot (4 (kb0 + j) + g, li) of each plane; hi
+    // in registers, lo in the wave's own LDS slots (read back only by the same lane)
+    bf16x8 qh[kAtaMaxBlocks];
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j) {
+        const int64_t slot = (int64_t)(4 * (kb0 + (j < kbn ? j : 0)) + g) * RP + li;
+        qh[j] = j < kbn ? qhi[slot] : bf16x8{};
+        sql[wave][j][lane] = j < kbn ? qlo[slot] : bf16x8{};
+    }
+
+    // columns n .. 32 nb - 1 of every panel row stay zero (phase 1 multiplies them)
+    const int tailc = (32 * nb - (int)n) / 8;
+    if ((int)threadIdx.x < kAtaPanel * tailc) {
+        const int row = threadIdx.x / tailc, cc = threadIdx.x % tailc;
+        *(u32x4 *)&sp[row * srow + (int)n + 8 * cc] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 zacc[kAtaMaxBlocks][2];
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j)
+        zacc[j][0] = zacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t npanels = (rows_here + kAtaPanel - 1) / kAtaPanel;
+    for (int64_t p = 0; p < npanels; ++p) {
+        store_panel(pf);
+        load_panel(p + 1, pf);  // past the last panel: all out of range, zeros, unused
+        __syncthreads();        // the panel is in LDS (and the previous one fully used)
+
+        // phase 1: this wave's share of Y = panel Q; lanes of tile rows 8..15 hold zeros
+        f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kAtaMaxBlocks; ++j) {
+            if (j < kbn) {
+                const bf16x8 a = *(const bf16x8 *)&sp[(li & 7) * srow + 32 * (kb0 + j) + 8 * g];
+                const bf16x8 az = li < kAtaPanel ? a : bf16x8{};
+                y = mfma(az, qh[j], y);
+                y = mfma(az, sql[wave][j][lane], y);
+            }
+        }
+        // D layout: lane (li, g) holds rows 4g..4g+3 of column li; rows 0..7 are g < 2
+        if (g < 2)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                sy[wave][(4 * g + v) * 16 + li] = y[v];
+        __syncthreads();  // partial Y written
+        if (threadIdx.x < kAtaPanel * 16) {
+            const int e = threadIdx.x, row = e / 16, col = e % 16;
+            float t = sy[0][e];
+#pragma unroll
+            for (int w = 1; w < kAtaWaves; ++w)
+                t += sy[w][e];
+            const __bf16 h = (__bf16)t, l = (__bf16)(t - (float)h);
+            syo[0][row / 4][col][row % 4] = __builtin_bit_cast(short, h);
+            syo[1][row / 4][col][row % 4] = __builtin_bit_cast(short, l);
+        }
+        __syncthreads();  // Y operand written
+
+        // phase 2: Z rows of this wave's blocks += panel^T (Y hi, Y lo)
+        const i16x4k bop = syo[g >> 1][g & 1][li];
+#pragma unroll
+        for (int j = 0; j < kAtaMaxBlocks; ++j) {
+            if (j < kbn) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c0 = 32 * (kb0 + j) + 16 * h;
+                    const i16x4 aop =
+                        lds_read_tr16(&sp[(4 * (g & 1) + (li >> 2)) * srow + c0 + 4 * (li & 3)]);
+                    zacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, zacc[j][h],
+                                                                           0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the panel and with Y
+    }
+
+    // D layout: lane (li, g) holds rows c0 + 4g .. + 3 of Z, column li
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j) {
+        if (j < kbn) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t c0 = 32 * (kb0 + j) + 16 * h + 4 * g;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (c0 + v < n && li < r)
+                        zpart[(c0 + v) * r + li] = zacc[j][h][v];
+            }
+        }
+    }
+}
+
+int ata_splits(int64_t batch, int64_t m, int64_t n, int r)
+{
+    if (r > 16 || n > kAtaMaxN || batch <= 0)
+        return 0;
+    int64_t s = kComputeUnits / batch;
+    s = s < 1 ? 1 : (s > kAtaMaxSplits ? kAtaMaxSplits : s);
+    const int64_t panels = (m + kAtaPanel - 1) / kAtaPanel;
+    return (int)(s < panels ? s : panels);
+}
+
 // ------------------------------------------------------------------ fp64 MFMA helpers
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -480,11 +690,14 @@ __device__ __forceinline__ void tile_times_rinv(const float *Mb, int64_t L, int 
 // D layout feed the Gram MFMA directly (A and B hold the same rows per lane
 // group and item, so the k order is consistent).  Only the upper tile pairs are
 // formed; the partial's lower off-diagonal tiles are written as zero.
+// nsum > 1 (without TRANSFORM): M is the first of nsum partial sums, pstride
+// floats apart; each element is their sum in order 0, 1, ..., written back
+// over the first (Msum, the same buffer) for the kernels after this one.
 template <int RP, bool TRANSFORM>
 __global__ void __launch_bounds__(kThreads)
 lr_gram_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int r,
                uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, size_t off_gram,
-               int blocks_per_mat)
+               int blocks_per_mat, float *Msum, int nsum, int64_t pstride)
 {
     constexpr int CT = RP / 16, NP = CT * (CT + 1) / 2;
     constexpr int WROWS = kGramRows / 4;  // rows per wave
@@ -518,7 +731,23 @@ lr_gram_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int r,
                 for (int v = 0; v < 4; ++v) {
                     const int64_t row = t0 + 4 * v + g;
                     const int col = 16 * ct + c;
-                    tile[ct][v] = (row < L && col < r) ? (double)Mb[row * r + col] : 0.0;
+                    float x = 0.0f;
+                    if (row < L && col < r) {
+                        const int64_t o = row * r + col;
+                        x = Mb[o];
+                        if (nsum > 1) {
+                            float pv[kMaxPartials];
+#pragma unroll
+                            for (int q = 1; q < kMaxPartials; ++q)
+                                pv[q] = q < nsum ? Mb[o + q * pstride] : 0.0f;
+#pragma unroll
+                            for (int q = 1; q < kMaxPartials; ++q)
+                                if (q < nsum)
+                                    x += pv[q];
+                            Msum[(int64_t)b * m_stride + o] = x;
+                        }
+                    }
+                    tile[ct][v] = (double)x;
                 }
         }
         int p = 0;
@@ -830,22 +1059,26 @@ lr_ops_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_t 
 
 // ------------------------------------------------------------------ host orchestration
 
+// nsum > 1: M (in the workspace) holds nsum partial sums of the matrix, L * r
+// floats apart; the first Gram kernel adds them up in place.
 template <int RP>
 hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_stride, int64_t L,
                     int r, uint8_t *ws, float *out, int64_t out_stride, bool ops, float *ru,
-                    hipStream_t st)
+                    hipStream_t st, int nsum = 1)
 {
     const int gblocks = (int)((L + kGramRows - 1) / kGramRows);
     const int64_t Lp_ops = round_up(L, 64);
     const int ablocks = (int)((Lp_ops + kApplyRows - 1) / kApplyRows);
     const unsigned ggrid = (unsigned)(gblocks * batch), agrid = (unsigned)(ablocks * batch);
     hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
-                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks);
+                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
+                       nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r);
     hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 1, Ly.off_r1, Ly.off_r1inv,
                        Ly.off_rinv, (float *)nullptr);
     hipLaunchKernelGGL((lr_gram_kernel<RP, true>), dim3(ggrid), dim3(kThreads), 0, st, M,
-                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks);
+                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
+                       (float *)nullptr, 1, (int64_t)0);
     hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 2, Ly.off_r1, Ly.off_r1inv,
                        Ly.off_rinv, ru);
@@ -858,7 +1091,7 @@ hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_s
 template <int RP>
 hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
 {
-    const Layout Ly = make_layout(a.m, a.n, a.r);
+    const Layout Ly = make_layout(a.batch, a.m, a.n, a.r);
     uint8_t *ws = (uint8_t *)a.ws;
     const float *mf = (const float *)(ws + Ly.off_mf);
     const int64_t mf_stride = (int64_t)(Ly.layer_bytes / 4);
@@ -883,16 +1116,26 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
             return e;
     }
     for (int t = 0; t < a.T; ++t) {
-        hipLaunchKernelGGL((lr_aq_kernel<RP, true>), dim3((unsigned)(aq_blocks * a.batch)),
-                           dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
-                           Ly.off_qops, Ly.off_yops, Ly.mp, Ly.np, aq_blocks);
-        hipLaunchKernelGGL((lr_aty_kernel<RP>), dim3((unsigned)(aty_blocks * a.batch)),
-                           dim3(kAtyThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
-                           Ly.off_yops, Ly.off_mf, Ly.mp, aty_blocks);
+        // Z = A^T (A Q): one pass over A with partial sums (r <= 16, n <= 3072), else two
+        if constexpr (RP == 16) {
+            if (Ly.splits > 0)
+                hipLaunchKernelGGL((lr_ata_kernel<RP>), dim3((unsigned)(Ly.splits * a.batch)),
+                                   dim3(kAtaThreads), 0, st, a.A, a.m, a.n, a.r, ws,
+                                   Ly.layer_bytes, Ly.off_qops, Ly.off_mf, Ly.np, Ly.splits,
+                                   Ly.split_rows);
+        }
+        if (Ly.splits == 0) {
+            hipLaunchKernelGGL((lr_aq_kernel<RP, true>), dim3((unsigned)(aq_blocks * a.batch)),
+                               dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
+                               Ly.off_qops, Ly.off_yops, Ly.mp, Ly.np, aq_blocks);
+            hipLaunchKernelGGL((lr_aty_kernel<RP>), dim3((unsigned)(aty_blocks * a.batch)),
+                               dim3(kAtyThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
+                               Ly.off_yops, Ly.off_mf, Ly.mp, aty_blocks);
+        }
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         if ((e = run_orth<RP>(Ly, a.batch, mf, mf_stride, a.n, a.r, ws, a.V, a.n * a.r, true,
-                              nullptr, st)) != hipSuccess)
+                              nullptr, st, Ly.splits > 1 ? Ly.splits : 1)) != hipSuccess)
             return e;
     }
     // final: P = A Q, (U, R_U) = orth(P), V = Q (already written)
@@ -909,7 +1152,7 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
 
 size_t lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int r)
 {
-    return make_layout(m, n, r).layer_bytes * (size_t)batch;
+    return make_layout(batch, m, n, r).layer_bytes * (size_t)batch;
 }
 
 hipError_t launch_lowrank(const LowrankArgs &a, hipStream_t st)

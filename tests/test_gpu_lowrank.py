@@ -78,7 +78,9 @@ def test_small_batch_parity(r, T):
     check(A, Q0, r, T, tag="small")
 
 
-@pytest.mark.parametrize("m,n,r", [(100, 72, 8), (33, 40, 16), (65, 136, 32), (1, 8, 1), (37, 520, 5)])
+# n = 3080 is past the one-pass A^T (A Q) (n <= 3072), so it covers the two-pass products at r <= 16
+@pytest.mark.parametrize("m,n,r", [(100, 72, 8), (33, 40, 16), (65, 136, 32), (1, 8, 1), (37, 520, 5),
+                                   (48, 3080, 16), (300, 3072, 16)])
 def test_ragged_shapes(m, n, r):
     if r > m:
         pytest.skip("r > m")
