@@ -89,6 +89,15 @@ def test_ragged_shapes(m, n, r):
     check(A, Q0, r, 2, tag="ragged")
 
 
+def test_large_batch_of_small_matrices():
+    """300 matrices: the one-pass A^T (A Q) then gives each matrix one work-group (one row
+    range, no partial sums to add); every 37th matrix is compared with the oracle."""
+    batch, m, n, r = 300, 40, 64, 4
+    A = lowrank_batch(batch, m, n, rank=6, sigma=0.1, seed=300)
+    Q0 = gaussian_q0(batch, n, r, seed=300)
+    check(A, Q0, r, 2, layers=list(range(0, batch, 37)) + [batch - 1], tag="large batch")
+
+
 @pytest.mark.parametrize("r", [8, 16, 32])
 def test_exact_rank_recovery(r):
     batch, m, n = 2, 256, 384
