@@ -620,6 +620,166 @@ lr_ata_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
     }
 }
 
+// The one-pass A^T (A Q) for r <= 8.  Only 8 of the 16 MFMA columns would carry
+// data, so they carry Q hi (columns 0..7) and Q lo (8..15) at once: a lane
+// of column li >= 8 loads column li - 8 of the lo plane.  Phase 1 then needs
+// one MFMA per block, Q lo leaves LDS, and the panel can be 16 rows (one full
+// row per wave to load, 6 x 16 bytes per lane in flight); phase 2 likewise
+// carries Y hi and Y lo as columns 0..7 and 8..15 of one K = 16 MFMA.  The two
+// halves of each product are added across lanes li and li + 8 (Y before the
+// cross-wave sum, Z once at the end).
+constexpr int kAta8Panel = 16;
+static_assert(kAtaWaves == kAta8Panel && kAtaMaxN == 8 * 64 * 6,
+              "each wave loads one full-width panel row in 6 16-byte loads per lane");
+
+template <int RP>
+__global__ void __launch_bounds__(kAtaThreads)
+lr_ata8_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
+               size_t layer_bytes, size_t off_qops, size_t off_z, int64_t np, int splits,
+               int64_t split_rows)
+{
+    static_assert(RP == 16, "columns 0..7 and 8..15 of the padded width carry hi and lo");
+    constexpr int kChunks = 6;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / splits, s = lid % splits;
+    uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    const bf16x8 *qhi = (const bf16x8 *)(wsb + off_qops);
+    const bf16x8 *qlo = qhi + (np / 8) * RP;
+    float *zpart = (float *)(wsb + off_z) + (size_t)s * n * r;
+
+    const int64_t row0 = (int64_t)s * split_rows;
+    const int64_t rows_here = m - row0 <= 0 ? 0 : (m - row0 < split_rows ? m - row0 : split_rows);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (int64_t)b * m * n + row0 * n, (uint32_t)(rows_here * n * 2));
+
+    __shared__ __attribute__((aligned(16))) uint16_t sp[kAta8Panel * kAtaSrowMax];
+    __shared__ float sy[kAtaWaves][kAta8Panel * 8];  // each wave's Y (hi + lo products added)
+    __shared__ i16x4k syo[16][4];  // [column: Y hi 0..7, Y lo 8..15][rows 4g..4g+3]
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
+    const int nb = (int)((n + 31) / 32);
+    const int nbw = (nb + kAtaWaves - 1) / kAtaWaves;
+    const int kb0 = wave * nbw;
+    const int kbn = nb - kb0 < nbw ? nb - kb0 : nbw;
+    const int srow = (int)round_up(32 * nb, 128) + 24;
+    const int cpr = (int)(n / 8);
+
+    // wave w loads row w of a panel: chunk k of a lane is columns 8 (lane + 64 k) .. + 7
+    auto load_panel = [&](int64_t p, u32x4 (&v)[kChunks]) {
+        const uint32_t base = (uint32_t)((p * kAta8Panel + wave) * n * 2);
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+            const int cc = lane + 64 * k;
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, cc < cpr ? base + (uint32_t)cc * 16 : kOOB, 0, 2 /*nt*/);
+        }
+    };
+    auto store_panel = [&](const u32x4 (&v)[kChunks]) {
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+            const int cc = lane + 64 * k;
+            if (cc < cpr)
+                *(u32x4 *)&sp[wave * srow + 8 * cc] = v[k];
+        }
+    };
+
+    u32x4 pf[kChunks];
+    load_panel(0, pf);
+
+    // packed Q operands of this wave's blocks: slot (4 (kb0 + j) + g, li & 7) of the hi
+    // plane in lanes li < 8, of the lo plane in lanes li >= 8
+    bf16x8 qp[kAtaMaxBlocks];
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j) {
+        const int64_t slot = (int64_t)(4 * (kb0 + (j < kbn ? j : 0)) + g) * RP + (li & 7);
+        qp[j] = j < kbn ? (li < 8 ? qhi[slot] : qlo[slot]) : bf16x8{};
+    }
+
+    const int tailc = (32 * nb - (int)n) / 8;
+    if ((int)threadIdx.x < kAta8Panel * tailc) {
+        const int row = threadIdx.x / tailc, cc = threadIdx.x % tailc;
+        *(u32x4 *)&sp[row * srow + (int)n + 8 * cc] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 zacc[kAtaMaxBlocks][2];
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j)
+        zacc[j][0] = zacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t npanels = (rows_here + kAta8Panel - 1) / kAta8Panel;
+    for (int64_t p = 0; p < npanels; ++p) {
+        store_panel(pf);
+        load_panel(p + 1, pf);  // past the last panel: all out of range, zeros, unused
+        __syncthreads();        // the panel is in LDS (and the previous one fully used)
+
+        // phase 1: D[row][c] = (panel Q hi)[row][c] for c < 8, (panel Q lo)[row][c - 8] above
+        f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kAtaMaxBlocks; ++j) {
+            if (j < kbn) {
+                const bf16x8 a = *(const bf16x8 *)&sp[li * srow + 32 * (kb0 + j) + 8 * g];
+                y = mfma(a, qp[j], y);
+            }
+        }
+        // D layout: lane (li, g) holds rows 4g..4g+3 of column li; hi + lo across li ^ 8
+        float ys[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            ys[v] = y[v] + __shfl_xor(y[v], 8);
+        if (li < 8)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                sy[wave][(4 * g + v) * 8 + li] = ys[v];
+        __syncthreads();  // partial Y written
+        if (threadIdx.x < kAta8Panel * 8) {
+            const int e = threadIdx.x, row = e / 8, col = e % 8;
+            float t = sy[0][e];
+#pragma unroll
+            for (int w = 1; w < kAtaWaves; ++w)
+                t += sy[w][e];
+            const __bf16 h = (__bf16)t, l = (__bf16)(t - (float)h);
+            syo[col][row / 4][row % 4] = __builtin_bit_cast(short, h);
+            syo[col + 8][row / 4][row % 4] = __builtin_bit_cast(short, l);
+        }
+        __syncthreads();  // Y operand written
+
+        // phase 2: D[c][j] = (panel^T Y hi)[c][j] for j < 8, (panel^T Y lo)[c][j - 8] above
+        const i16x4k bop = syo[li][g];
+#pragma unroll
+        for (int j = 0; j < kAtaMaxBlocks; ++j) {
+            if (j < kbn) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c0 = 32 * (kb0 + j) + 16 * h;
+                    const i16x4 aop =
+                        lds_read_tr16(&sp[(4 * g + (li >> 2)) * srow + c0 + 4 * (li & 3)]);
+                    zacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, zacc[j][h],
+                                                                           0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the panel and with Y
+    }
+
+    // D layout: lane (li, g) holds rows c0 + 4g .. + 3 of Z, column li; hi + lo across li ^ 8
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j) {
+        if (j < kbn) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t c0 = 32 * (kb0 + j) + 16 * h + 4 * g;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float zs = zacc[j][h][v] + __shfl_xor(zacc[j][h][v], 8);
+                    if (c0 + v < n && li < r)
+                        zpart[(c0 + v) * r + li] = zs;
+                }
+            }
+        }
+    }
+}
+
 int ata_splits(int64_t batch, int64_t m, int64_t n, int r)
 {
     if (r > 16 || n > kAtaMaxN || batch <= 0)
@@ -1119,10 +1279,10 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
         // Z = A^T (A Q): one pass over A with partial sums (r <= 16, n <= 3072), else two
         if constexpr (RP == 16) {
             if (Ly.splits > 0)
-                hipLaunchKernelGGL((lr_ata_kernel<RP>), dim3((unsigned)(Ly.splits * a.batch)),
-                                   dim3(kAtaThreads), 0, st, a.A, a.m, a.n, a.r, ws,
-                                   Ly.layer_bytes, Ly.off_qops, Ly.off_mf, Ly.np, Ly.splits,
-                                   Ly.split_rows);
+                hipLaunchKernelGGL((a.r <= 8 ? lr_ata8_kernel<RP> : lr_ata_kernel<RP>),
+                                   dim3((unsigned)(Ly.splits * a.batch)), dim3(kAtaThreads), 0, st,
+                                   a.A, a.m, a.n, a.r, ws, Ly.layer_bytes, Ly.off_qops,
+                                   Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows);
         }
         if (Ly.splits == 0) {
             hipLaunchKernelGGL((lr_aq_kernel<RP, true>), dim3((unsigned)(aq_blocks * a.batch)),
