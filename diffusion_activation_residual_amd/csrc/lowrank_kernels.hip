@@ -8,7 +8,10 @@
 // Tall-skinny products on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 // A is bf16 and exact; the skinny operand (Q or Y, fp32) is split into
 // hi = bf16(x) and lo = bf16(x - hi) and both halves are multiplied, so the
-// product carries about 16 bits of the skinny operand instead of 8.
+// product carries about 16 bits of the skinny operand instead of 8.  For
+// r <= 16 and n <= 3072, Y = A Q and Z = A^T Y run as one pass over A
+// (lr_ata_kernel, lr_ata8_kernel for r <= 8); otherwise as two (lr_aq_kernel,
+// lr_aty_kernel).
 //
 // orth() is Cholesky-QR applied twice: Gram matrix G = M^T M accumulated in
 // fp64 from fp32 rows, r x r Cholesky and triangular inverse in fp64 in LDS,
