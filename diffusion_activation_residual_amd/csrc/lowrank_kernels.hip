@@ -455,10 +455,10 @@ lr_aty_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
 // LDS slots) and its rows of Z (48) for the whole kernel, so the only memory
 // loads in the loop are the panels: every wave keeps its share of the next
 // panel (3 x 16 bytes per lane) in flight from the moment the current one is
-// in LDS.  Vector loads return
-// in issue order, so any other load issued behind a panel would wait for it.
-// Z is written once per work-group as one fp32 [n][r] partial; the Gram kernel
-// sums the `splits` partials in a fixed order.  RP = 16 only.
+// in LDS.  Vector loads return in issue order, so any other load issued
+// behind a panel would wait for it.  Z is written once per work-group as one
+// fp32 [n][r] partial; the Gram kernel sums the `splits` partials in a fixed
+// order.  RP = 16 only.
 constexpr int kAtaWaves = 16;
 constexpr int kAtaThreads = 64 * kAtaWaves;
 constexpr int kAtaPanel = 8;                           // rows per panel
