@@ -148,15 +148,19 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
         RU = torch.empty(batch, r, r, device=dev)
         ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(batch, m, n, r), dtype=torch.uint8,
                          device=dev)
-        cfz.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            cfz.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 1e3 / reps
+        def timed(iters):
+            cfz.cfz_lowrank(batch, m, n, r, iters, A, Q0, U, V, RU, ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                cfz.cfz_lowrank(batch, m, n, r, iters, A, Q0, U, V, RU, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1e3 / reps
+
+        t1 = timed(T - 1) if T >= 2 else None
+        t = timed(T)  # last, so that U, V, R_U hold the T-iteration result
         # algorithmic bytes: A read once, Q0 read, U, V, R_U written
         alg = batch * (2 * m * n + 4 * n * r + 4 * (m + n) * r + 4 * r * r)
         useful_flop = batch * 2 * m * n * r * (2 * T + 1)
@@ -170,6 +174,14 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
             "A_passes": passes,
             "achieved_GB/s_all_passes": round(passes * batch * 2 * m * n / t / 1e9, 1),
             "useful_TFLOP/s": round(useful_flop / t / 1e12, 2)}
+        if t1 is not None:
+            # one iteration (A^T (A Q) and the orthogonalisation of Z) = the difference
+            # between T and T - 1 iterations
+            it, reads = t - t1, (passes - 1) // T
+            out["per_rank"][str(r)].update({
+                "us_per_iteration": round(it * 1e6, 1),
+                "A_reads_per_iteration": reads,
+                "A_GB/s_in_iteration": round(reads * batch * 2 * m * n / it / 1e9, 1)})
         del ws
     return out
 
