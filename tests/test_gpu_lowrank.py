@@ -89,6 +89,17 @@ def test_ragged_shapes(m, n, r):
     check(A, Q0, r, 2, tag="ragged")
 
 
+@pytest.mark.parametrize("r", [8, 16])
+def test_cogvideox_shaped_matrices(r):
+    """4 matrices of 4388 x 1920 (the CogVideoX-2b share's K/V shape): the one-pass
+    A^T (A Q) with 8 row ranges of 560 rows per matrix, the last one ragged; matrices 0
+    and 3 compared with the oracle."""
+    batch, m, n = 4, 4388, 1920
+    A = lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=4388 + r)
+    Q0 = gaussian_q0(batch, n, r, seed=1920 + r)
+    check(A, Q0, r, 2, layers=[0, 3], tag=f"cogvideox-shaped r={r}")
+
+
 def test_large_batch_of_small_matrices():
     """300 matrices: the one-pass A^T (A Q) then gives each matrix one work-group (one row
     range, no partial sums to add); every 37th matrix is compared with the oracle."""
