@@ -419,23 +419,27 @@ def test_cogvideox_full_size_sampled_rows(bits, group):
     _batched_rows_parity("cogvideox", bits, group, sp.steps, sl, f"cogvideox b{bits}")
 
 
-@pytest.mark.parametrize("bits,group", [(4, 64), (2, 32)])
-def test_cogvideox_full_size_per_layer_launches(bits, group):
+@pytest.mark.parametrize("bits,group,sb,steps", [(4, 64, False, 50), (2, 32, False, 50),
+                                                  (4, 64, True, 12)])
+def test_cogvideox_full_size_per_layer_launches(bits, group, sb, steps):
     """CogVideoX-2b share in the benchmark's launch configuration: 30 layers x {K, V} of
     4388 x 1920, one grouped compress and one grouped decode launch per layer, 49 compressed
-    steps; layers 0 and 29 (tensors 0, 1, 58, 59) compared with the oracle every step."""
+    steps (11 with bf16 state); layers 0 and 29 (tensors 0, 1, 58, 59) compared with the
+    oracle every step."""
     sp = SPECS["cogvideox"]
     st = AR1Stream.from_spec(sp, seed=2, device=DEV)
     picks = [0, 1, 58, 59]
-    say(f"[gpu] cogvideox per-layer launches int{bits} g{group}, tensors {picks}")
+    say(f"[gpu] cogvideox per-layer launches int{bits} g{group} bf16 state={sb}, tensors {picks}")
     x = st.next()
     n = sp.rows * sp.cols
-    gs = [cfz.Sender(sp.rows, sp.cols, bits, group, x0=x[i].contiguous()) for i in range(sp.tensors)]
-    gr = [cfz.Receiver(sp.rows, sp.cols, bits, group, x0=x[i].contiguous())
+    gs = [cfz.Sender(sp.rows, sp.cols, bits, group, x0=x[i].contiguous(), state_bf16=sb)
           for i in range(sp.tensors)]
-    os_ = {i: oracle.Sender(n, bits, group, oracle.DELTA, x0=u16(x[i])) for i in picks}
-    or_ = {i: oracle.Receiver(n, bits, group, x0=u16(x[i])) for i in picks}
-    for t in range(1, sp.steps):
+    gr = [cfz.Receiver(sp.rows, sp.cols, bits, group, x0=x[i].contiguous(), state_bf16=sb)
+          for i in range(sp.tensors)]
+    os_ = {i: oracle.Sender(n, bits, group, oracle.DELTA, x0=u16(x[i]), state_bf16=sb)
+           for i in picks}
+    or_ = {i: oracle.Receiver(n, bits, group, x0=u16(x[i]), state_bf16=sb) for i in picks}
+    for t in range(1, steps):
         x = st.next()
         for l in range(sp.tensors // 2):
             pair = (2 * l, 2 * l + 1)
