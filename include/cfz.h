@@ -170,7 +170,10 @@ cfz_status cfz_decompress_group(int32_t count, cfz_state *const *receivers,
                                 const uint8_t *const *codes, const float *const *scales,
                                 uint16_t *const *xhat_bf16, void *hip_stream);
 
-/* Workspace for cfz_lowrank, in bytes, or 0 if the sizes are invalid. */
+/* Workspace for cfz_lowrank, in bytes, or 0 if the sizes are invalid.  Not
+ * monotone in batch (a small batch splits each matrix into more row ranges, each
+ * with its own partial sums), so query it with each call's own sizes; a call
+ * given less returns CFZ_ERR_WORKSPACE and enqueues nothing. */
 size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t r);
 
 /* Algorithm 3 (Subspace Iteration, rank r) on `batch` independent matrices
