@@ -694,7 +694,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # the codec's arithmetic: residual, scale division and updates in fp32
+        "activation_dtype": "bf16",  # what the metric counts: bf16 activation bytes
+        "state_dtype": "f32",  # carried error and base (the bf16_state leg holds them in bf16)
         "data": "synthetic (seeded AR(1) bf16 activations, alpha 0.98, LogNormal(0,0.5) channel "
                 "scales, 1% outlier channels x20)",
         "config": {"workload": workload, "tensors": T, "rows": rows, "cols": cols, "bits": bits,

@@ -80,7 +80,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // One 64-byte record per tensor: a work-group reads its tensor's record with a
 // single scalar load (blockIdx.y is the tensor, blockIdx.x the block within it;
-// blocks past a smaller tensor's end exit at once).
+// work-groups past a smaller tensor's last block have nothing to do).
 struct CompressRec {
     const uint16_t *x;
     uint16_t *prev;
@@ -187,8 +187,10 @@ __device__ __forceinline__ float group_max4(float v)
 
 // ---------------------------------------------------------------- compress
 
-template <int BITS, int G, int MODE, bool SB, int UNROLL, int MAXT>
-__global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTable<MAXT> tab)
+// Block `blk` (< the tensor's block count) of one tensor's compress: quads
+// blk * kBlock * UNROLL + threadIdx.x + u * kBlock, u < UNROLL, those below nquads.
+template <int BITS, int G, int MODE, bool SB, int UNROLL>
+__device__ __forceinline__ void compress_block(const CompressRec &rec, int64_t blk)
 {
     constexpr int LANES = G / 4;
     constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
@@ -197,17 +199,14 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
     constexpr bool USE_BASE = (MODE == kLiteral || MODE == kOff);
     constexpr bool USE_ERR = (MODE == kDelta || MODE == kLiteral);
 
-    const CompressRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
     const int64_t nq = rec.nquads;
-    if ((int64_t)blockIdx.x * (kBlock * UNROLL) >= nq)
-        return;  // this tensor is smaller than the grid's widest one
     const uint16_t *__restrict__ x = rec.x;
     uint16_t *__restrict__ prev = rec.prev;
     void *__restrict__ base = rec.base;
     void *__restrict__ err = rec.err;
     uint8_t *__restrict__ codes = rec.codes;
     float *__restrict__ scales = rec.scales;
-    const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
+    const int64_t q0 = blk * (kBlock * UNROLL) + threadIdx.x;
 
     u32x2 xv[UNROLL], pv[UNROLL];
     Quad<SB> sv[UNROLL], ev[UNROLL];
@@ -288,21 +287,31 @@ __global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTabl
     }
 }
 
+// Grid (gx, tensors, gz): work-group (x, y, z) takes block x + gx * z of tensor y;
+// gz > 1 only for a tensor with more blocks than one grid row holds.
+__device__ __forceinline__ int64_t grid_block() { return blockIdx.x + (int64_t)gridDim.x * blockIdx.z; }
+
+template <int BITS, int G, int MODE, bool SB, int UNROLL, int MAXT>
+__global__ void __launch_bounds__(kBlock) cfz_compress_kernel(const CompressTable<MAXT> tab)
+{
+    const CompressRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
+    const int64_t blk = grid_block();
+    if (blk * (kBlock * UNROLL) < rec.nquads)  // else past a smaller tensor's last block
+        compress_block<BITS, G, MODE, SB, UNROLL>(rec, blk);
+}
+
 // ---------------------------------------------------------------- decode
 
-template <int BITS, int G, bool SB, int UNROLL, int MAXT>
-__global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MAXT> tab)
+template <int BITS, int G, bool SB, int UNROLL>
+__device__ __forceinline__ void decode_block(const DecodeRec &rec, int64_t blk)
 {
     constexpr int LANES = G / 4;
-    const DecodeRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
     const int64_t nq = rec.nquads;
-    if ((int64_t)blockIdx.x * (kBlock * UNROLL) >= nq)
-        return;
     const uint8_t *__restrict__ codes = rec.codes;
     const float *__restrict__ scales = rec.scales;
     void *__restrict__ base = rec.base;
     uint16_t *__restrict__ xhat = rec.xhat;
-    const int64_t q0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
+    const int64_t q0 = blk * (kBlock * UNROLL) + threadIdx.x;
 
     uint32_t word[UNROLL];
     float sc[UNROLL];
@@ -340,6 +349,15 @@ __global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MA
             st_nt(u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])}, (u32x2 *)(xhat + 4 * q));
         }
     }
+}
+
+template <int BITS, int G, bool SB, int UNROLL, int MAXT>
+__global__ void __launch_bounds__(kBlock) cfz_decode_kernel(const DecodeTable<MAXT> tab)
+{
+    const DecodeRec &rec = tab.t[MAXT == 1 ? 0 : blockIdx.y];
+    const int64_t blk = grid_block();
+    if (blk * (kBlock * UNROLL) < rec.nquads)
+        decode_block<BITS, G, SB, UNROLL>(rec, blk);
 }
 
 // ---------------------------------------------------------------- warm-up
@@ -412,6 +430,21 @@ static inline unsigned grid_for(int64_t items, int64_t per_block)
 // Launches over fewer quads than this ramp up too briefly for one quad per lane
 // to keep enough bytes in flight; they take four quads per lane instead.
 constexpr int64_t kBigLaunchQuads = (int64_t)4 << 20;
+// The grid's x dimension times kBlock threads must stay below 2^32.
+constexpr int64_t kMaxGridX = (int64_t)1 << 23;
+
+// Grid for tensors of at most `widest` quads: one work-group per block, in rows of
+// at most kMaxGridX work-groups (z) when one row cannot hold them.
+static bool plain_grid(int64_t widest, int unroll, int count, dim3 *grid)
+{
+    const int64_t nblk = (widest + kBlock * unroll - 1) / (kBlock * unroll);
+    const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
+    const int64_t gz = (nblk + gx - 1) / gx;
+    if (gz > 65535)
+        return false;
+    *grid = dim3((unsigned)gx, (unsigned)count, (unsigned)gz);
+    return true;
+}
 
 template <int BITS, int G, int MODE, bool SB, int UNROLL, int MAXT>
 static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t st)
@@ -424,11 +457,11 @@ static hipError_t compress_chunk(const CompressItem *it, int count, hipStream_t 
                                it[i].scales, nq, 0};
         widest = nq > widest ? nq : widest;
     }
-    const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
-    if (blocks > INT32_MAX)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, SB, UNROLL, MAXT>),
-                       dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
+    dim3 grid;
+    if (widest == 0 || !plain_grid(widest, UNROLL, count, &grid))
+        return widest == 0 ? hipSuccess : hipErrorInvalidValue;
+    hipLaunchKernelGGL((cfz_compress_kernel<BITS, G, MODE, SB, UNROLL, MAXT>), grid, dim3(kBlock),
+                       0, st, tab);
     return hipGetLastError();
 }
 
@@ -504,11 +537,11 @@ static hipError_t decode_chunk(const DecodeItem *it, int count, hipStream_t st)
         tab.t[i] = DecodeRec{it[i].codes, it[i].scales, it[i].base, it[i].xhat, nq, {0, 0, 0}};
         widest = nq > widest ? nq : widest;
     }
-    const int64_t blocks = (widest + kBlock * UNROLL - 1) / (kBlock * UNROLL);
-    if (blocks > INT32_MAX)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, SB, UNROLL, MAXT>),
-                       dim3((unsigned)blocks, (unsigned)count), dim3(kBlock), 0, st, tab);
+    dim3 grid;
+    if (widest == 0 || !plain_grid(widest, UNROLL, count, &grid))
+        return widest == 0 ? hipSuccess : hipErrorInvalidValue;
+    hipLaunchKernelGGL((cfz_decode_kernel<BITS, G, SB, UNROLL, MAXT>), grid, dim3(kBlock), 0, st,
+                       tab);
     return hipGetLastError();
 }
 

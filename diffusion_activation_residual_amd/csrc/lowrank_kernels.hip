@@ -855,10 +855,12 @@ __device__ __forceinline__ void tile_times_rinv(const float *Mb, int64_t L, int 
 // formed; the partial's lower off-diagonal tiles are written as zero.
 // nsum > 1 (without TRANSFORM): M is the first of nsum partial sums, pstride
 // floats apart; each element is their sum in order 0, 1, ..., written back
-// over the first (Msum, the same buffer) for the kernels after this one.
+// over the first (Msum, the same buffer) for the kernels after this one.  M and
+// Msum alias, so neither is declared restrict; each element is read by the one
+// thread that then writes it.
 template <int RP, bool TRANSFORM>
 __global__ void __launch_bounds__(kThreads)
-lr_gram_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int r,
+lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
                uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, size_t off_gram,
                int blocks_per_mat, float *Msum, int nsum, int64_t pstride)
 {
@@ -1123,12 +1125,15 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
 // Q = M Rinv on fp64 MFMA, 16-row tiles per wave, then through LDS so that the
 // fp32 output is written row by row and every operand slot (8 rows of one
 // column) is one 16-byte store per plane.  Rows L..Lp-1 of the operand layout
-// are written as zeros; columns r..RP-1 are zero.
+// are written as zeros; columns r..RP-1 are zero.  M and out may be the same
+// buffer (Q0 passed as V at T = 0), so neither is restrict: a wave reads its
+// 16-row tile in full before it writes that tile's rows, and no other wave
+// touches them.
 template <int RP>
 __global__ void __launch_bounds__(kThreads)
-lr_apply_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_t Lp, int r,
+lr_apply_kernel(const float *M, int64_t m_stride, int64_t L, int64_t Lp, int r,
                 uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, bool ops,
-                size_t off_ops, float *__restrict__ out, int64_t out_stride, int blocks_per_mat)
+                size_t off_ops, float *out, int64_t out_stride, int blocks_per_mat)
 {
     constexpr int CT = RP / 16;
     constexpr int WROWS = kApplyRows / 4;

@@ -147,6 +147,10 @@ cfz_status cfz_compress(cfz_state *sender, const uint16_t *x_bf16, uint8_t *code
  * q != 0 (a zero code leaves the base bit-identical; with bf16 state the fma
  * result is rounded once to bf16), and optionally write the new base rounded to
  * bf16 (nearest even) into xhat_bf16 (may be NULL).
+ * (paper: abstract -- only compressed residuals are transmitted, so the receiver
+ * rebuilds the activation by adding each decoded residual to its base;
+ * reproducibility table, "Dataset Splits" -- that base starts from the
+ * uncompressed warm-up activation.)
  * Errors: CFZ_ERR_NULL, CFZ_ERR_ALIGN, CFZ_ERR_MODE (sender state), CFZ_ERR_HIP. */
 cfz_status cfz_decompress(cfz_state *receiver, const uint8_t *codes, const float *scales,
                           uint16_t *xhat_bf16, void *hip_stream);
@@ -210,8 +214,9 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
  * with the same kernel (fp32, v_mfma_f32_16x16x4_f32), so with the same
  * factors their reconstructions agree bit for bit.
  * Layouts: x, prev, xhat bf16 and err, base fp32, all [batch][m][n]; U, V, RU
- * as for cfz_lowrank.  Sizes as for cfz_lowrank, plus batch * ceil(m / 64) *
- * ceil(n / 128) < 2^31.  Every pointer 16-byte aligned; the caller owns all
+ * as for cfz_lowrank.  Sizes as for cfz_lowrank, plus two launch-size limits:
+ * batch * ceil(m / 256) * ceil(n / 256) < 2^31 and batch * m * n / 1024 < 2^31
+ * (integer division).  Every pointer 16-byte aligned; the caller owns all
  * memory.  Calls are asynchronous on hip_stream; tensors of one state must not
  * be used on two streams at once. */
 
