@@ -67,6 +67,8 @@ def _load():
         "cfz_decompress_group": ([i32, p, p, p, p, p], i32),
         "cfz_lowrank_workspace_bytes": ([i64, i64, i64, i32], sz),
         "cfz_lowrank": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, sz, p], i32),
+        "cfz_lowrank_noalloc": ([i64, i64, i64, i32, i32, p, p, p, p, p, p], i32),
+        "cfz_lowrank_noalloc_max_bytes": ([], sz),
         "cfz_lowrank_ef_workspace_bytes": ([i64, i64, i64, i32], sz),
         "cfz_lowrank_ef_warmup": ([i64, p, p, p, p, p], i32),
         "cfz_lowrank_ef_compress": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p], i32),
@@ -303,6 +305,17 @@ def cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, workspace, ws_bytes=None, st
     _need(workspace, ws_bytes, "workspace")
     _check(_lib.cfz_lowrank(batch, m, n, r, T, _bf16_ptr(A), _ptr(Q0), _ptr(U), _ptr(V),
                             _ptr(RU), _ptr(workspace), ws_bytes, _stream(stream)), "cfz_lowrank")
+
+
+def cfz_lowrank_noalloc_max_bytes() -> int:
+    return _lib.cfz_lowrank_noalloc_max_bytes()
+
+
+def cfz_lowrank_noalloc(batch, m, n, r, T, A, Q0, U, V, RU, stream=None) -> None:
+    """cfz_lowrank on the library's built-in scratch: no workspace argument, no allocation."""
+    _check_lowrank(batch, m, n, r, A, Q0, U, V, RU)
+    _check(_lib.cfz_lowrank_noalloc(batch, m, n, r, T, _bf16_ptr(A), _ptr(Q0), _ptr(U), _ptr(V),
+                                    _ptr(RU), _stream(stream)), "cfz_lowrank_noalloc")
 
 
 def cfz_lowrank_ef_workspace_bytes(batch, m, n, r) -> int:

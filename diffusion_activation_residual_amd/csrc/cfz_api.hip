@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "cfz.h"
@@ -440,6 +441,84 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
                     ws ? ws_bytes : (size_t)0);
     if (((uintptr_t)ws & 255u) != 0)
         return fail(CFZ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    cfz::LowrankArgs a{batch, m, n, r, T, A, Q0, U, V, RU, ws};
+    hipError_t e = cfz::launch_lowrank(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "low-rank launch");
+    return CFZ_OK;
+}
+
+}  // extern "C"
+
+// ---- the subspace iteration without a caller workspace ---------------------
+//
+// For callers that cannot allocate device memory (code under graph capture, tight
+// serving loops): the workspace is this file-scope device array, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side stand-in,
+// not a device address, so every use goes through the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // covers 57 x 1024 x 3072 at any r
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // per device, filled on first use
+
+// The current device's copy of `scratch`, or an error status.
+cfz_status scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CFZ_ERR_HIP, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || ((uintptr_t)p & 255u) != 0)
+            return fail(CFZ_ERR_HIP, "scratch array at an unusable address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CFZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cfz_lowrank_noalloc_max_bytes(void) { return kScratchBytes; }
+
+cfz_status cfz_lowrank_noalloc(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                               const uint16_t *A, const float *Q0, float *U, float *V, float *RU,
+                               void *stream)
+{
+    cfz_status st = check_lowrank_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (T < 0)
+        return fail(CFZ_ERR_SHAPE, "iterations T = %d", T);
+    if (batch == 0)
+        return CFZ_OK;
+    if (!A || !Q0 || !U || !V || !RU)
+        return fail(CFZ_ERR_NULL, "A, Q0, U, V and RU are required");
+    if (!aligned16(A) || !aligned16(Q0) || !aligned16(U) || !aligned16(V) || !aligned16(RU))
+        return fail(CFZ_ERR_ALIGN, "A, Q0, U, V and RU must be 16-byte aligned");
+    const size_t need = cfz::lowrank_workspace_bytes(batch, m, n, r);
+    if (need > kScratchBytes)
+        return fail(CFZ_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of workspace, beyond the %zu-byte built-in "
+                    "scratch; use cfz_lowrank with a caller workspace", need, kScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != CFZ_OK)
+        return st;
     cfz::LowrankArgs a{batch, m, n, r, T, A, Q0, U, V, RU, ws};
     hipError_t e = cfz::launch_lowrank(a, (hipStream_t)stream);
     if (e != hipSuccess)

@@ -203,6 +203,23 @@ cfz_status cfz_lowrank(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T
                        const uint16_t *A_bf16, const float *Q0, float *U, float *V, float *RU,
                        void *workspace, size_t ws_bytes, void *hip_stream);
 
+/* cfz_lowrank without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * hipMalloc).  Same arguments, results and errors as cfz_lowrank, bit for bit;
+ * the workspace is a device array built into the library, one copy per GPU,
+ * cfz_lowrank_noalloc_max_bytes() bytes (64 MiB: enough for 57 matrices of
+ * 1024 x 3072 at any r), held until the process ends.  Sizes whose
+ * cfz_lowrank_workspace_bytes exceeds it return CFZ_ERR_WORKSPACE before any
+ * device work.  The call itself allocates nothing; its first call on a device
+ * looks up that device's copy (hipGetSymbolAddress).  Every call on one GPU
+ * uses the same array and leaves its contents behind (nothing in it needs to
+ * start at zero), so calls that may run at the same time on one GPU -- on two
+ * streams, or from two threads -- race and must be serialised by the caller. */
+cfz_status cfz_lowrank_noalloc(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                               const uint16_t *A_bf16, const float *Q0, float *U, float *V,
+                               float *RU, void *hip_stream);
+size_t cfz_lowrank_noalloc_max_bytes(void);
+
 /* ---- The rank-r compressor inside the error-feedback loop ----------------
  * The pages send step-wise residuals with error feedback (abstract) and give
  * the subspace iteration as a compressor (Algorithm 3).  Combined like the

@@ -14,7 +14,7 @@ MISALIGNED = 0x10008
 
 def test_library_exports_every_declared_function():
     names = cfz.header_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
     assert cfz.cfz_abi_version() == 3
@@ -227,6 +227,29 @@ def test_group_validation_without_launching():
     finally:
         for h in (a, b, lit, rcv, half):
             cfz.cfz_state_destroy(h)
+
+
+def test_noalloc_lowrank_rejects_sizes_beyond_its_scratch():
+    """The workspace-free subspace iteration refuses, on the host, sizes whose workspace
+    would not fit its built-in scratch, and validates like cfz_lowrank otherwise; nothing
+    here reaches a device (validation fails first)."""
+    lib = cfz._lib
+    cap = cfz.cfz_lowrank_noalloc_max_bytes()
+    assert cap == 64 << 20
+    assert cfz.cfz_lowrank_workspace_bytes(57, 1024, 3072, 16) <= cap
+    big = (114, 1024, 3072, 16)
+    assert cfz.cfz_lowrank_workspace_bytes(*big) > cap
+    args = (ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)
+    st = lib.cfz_lowrank_noalloc(*big, 2, *args)
+    assert st == cfz.CFZ_ERR_WORKSPACE and "scratch" in cfz.cfz_last_error()
+    assert lib.cfz_lowrank_noalloc(2, 64, 128, 33, 2, *args) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_lowrank_noalloc(2, 64, 128, 8, -1, *args) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_lowrank_noalloc(2, 64, 128, 8, 2, None, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                                   None) == cfz.CFZ_ERR_NULL
+    assert lib.cfz_lowrank_noalloc(2, 64, 128, 8, 2, MISALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                                   ALIGNED, None) == cfz.CFZ_ERR_ALIGN
+    assert lib.cfz_lowrank_noalloc(0, 64, 128, 8, 2, None, None, None, None, None,
+                                   None) == cfz.CFZ_OK
 
 
 def test_binding_rejects_undersized_tensors_before_any_launch():
