@@ -13,10 +13,14 @@
 // (lr_ata_kernel, lr_ata8_kernel for r <= 8); otherwise as two (lr_aq_kernel,
 // lr_aty_kernel).
 //
-// orth() is Cholesky-QR applied twice: Gram matrix G = M^T M accumulated in
-// fp64 from fp32 rows, r x r Cholesky and triangular inverse in fp64 in LDS,
-// then M R^-1 row by row.  A pivot <= 1e-13 * trace(G) / r (or not finite)
-// drops the column: zero Q column, zero R row and column.
+// orth() is Cholesky-QR: Gram matrix G = M^T M accumulated in fp64 from fp32
+// rows, r x r Cholesky and triangular inverse in fp64, then M R^-1 row by row.
+// A second pass (CholQR2) runs for a matrix only when the first cannot deliver
+// fp32 orthogonality: its loss of orthogonality is about kappa(M)^2 u_fp64, so
+// the second pass is taken when the estimate ||R1||_F ||R1^-1||_F >= kappa(M)
+// exceeds 2^14.5 (kappa^2 u_fp64 > u_fp32); the other matrices of the batch
+// leave its two launches at once.  A pivot <= 1e-13 * trace(G) / r (or not
+// finite) drops the column: zero Q column, zero R row and column.
 //
 // Skinny operands live in the workspace in "operand layout": hi and lo bf16
 // planes of shape [L/8][RP][8], where RP = 16 or 32 is r padded to the MFMA
@@ -43,6 +47,10 @@ constexpr int kGramRows = 256;    // rows of M per Gram work-group (64 per wave)
 constexpr int kApplyRows = 256;   // rows of M per apply work-group (64 per wave)
 constexpr int kCholThreads = 64;  // the r x r factorisation runs on one wavefront
 constexpr int kMaxPartials = 8;   // partial sums of Z the Gram kernel adds up
+// Second Cholesky-QR pass when ||R1||_F^2 ||R1^-1||_F^2 exceeds 2^29: the first
+// pass's loss of orthogonality, about kappa^2 u_fp64 = kappa^2 2^-53, could then
+// exceed the fp32 output's own rounding, 2^-24.
+constexpr double kTwoPassKappa2 = 536870912.0;  // 2^29
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -68,7 +76,7 @@ struct Layout {
     int64_t gram_blocks;        // max over (m, n) of row blocks of the Gram kernel
     int splits;                 // row ranges of the one-pass A^T (A Q); 0: two passes
     int64_t split_rows;         // rows per range, a multiple of the 16-row panel
-    size_t off_qops, off_yops, off_mf, off_gram, off_r1, off_r1inv, off_rinv;
+    size_t off_qops, off_yops, off_mf, off_gram, off_r1, off_r1inv, off_rinv, off_flag;
     size_t layer_bytes;
 };
 
@@ -102,6 +110,7 @@ Layout make_layout(int64_t batch, int64_t m, int64_t n, int r)
     L.off_r1 = off;   off = align256(off + (size_t)L.rp * L.rp * 8);
     L.off_r1inv = off; off = align256(off + (size_t)L.rp * L.rp * 8);
     L.off_rinv = off; off = align256(off + (size_t)L.rp * L.rp * 8);
+    L.off_flag = off; off = align256(off + sizeof(int32_t));
     L.layer_bytes = off;
     return L;
 }
@@ -858,11 +867,13 @@ __device__ __forceinline__ void tile_times_rinv(const float *Mb, int64_t L, int 
 // over the first (Msum, the same buffer) for the kernels after this one.  M and
 // Msum alias, so neither is declared restrict; each element is read by the one
 // thread that then writes it.
+// With TRANSFORM (the second pass) the work-groups of a matrix whose first pass
+// sufficed (flag 0 at off_flag) return at once.
 template <int RP, bool TRANSFORM>
 __global__ void __launch_bounds__(kThreads)
 lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
                uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_rinv, size_t off_gram,
-               int blocks_per_mat, float *Msum, int nsum, int64_t pstride)
+               int blocks_per_mat, float *Msum, int nsum, int64_t pstride, size_t off_flag)
 {
     constexpr int CT = RP / 16, NP = CT * (CT + 1) / 2;
     constexpr int WROWS = kGramRows / 4;  // rows per wave
@@ -870,6 +881,10 @@ lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
     const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
     const float *Mb = M + (int64_t)b * m_stride;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    if constexpr (TRANSFORM) {
+        if (*(const int32_t *)(wsb + off_flag) == 0)
+            return;
+    }
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, c = lane & 15;
     __shared__ double sacc[4][RP * RP];
 
@@ -946,16 +961,29 @@ lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
 // G = R^T R (R upper, positive diagonal) in fp64 with lane j holding column j in
 // registers (pivots and multipliers broadcast with readlane), and inverts R by
 // back substitution, again one column per lane.
-// pass 1: store R1 and R1^-1.  pass 2: store (R1^-1 R2^-1) and, when ru_out is
-// given, R = R2 R1 as fp32 [r][r].
+// pass 1: store R1 and R1^-1, R1^-1 also as the final R^-1, and decide whether
+// the matrix needs the second pass (flag at off_flag).  pass 2: for a flagged
+// matrix, overwrite the final R^-1 with (R1^-1 R2^-1) and, when ru_out is
+// given, store R = R2 R1 as fp32 [r][r]; for the others only R = R1.
 template <int RP>
 __global__ void __launch_bounds__(kCholThreads)
 lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, int gram_blocks,
                int r, int pass, size_t off_r1, size_t off_r1inv, size_t off_rinv,
-               float *__restrict__ ru_out)
+               float *__restrict__ ru_out, size_t off_flag)
 {
     const int b = blockIdx.x;
     uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    int32_t *flag = (int32_t *)(wsb + off_flag);
+    if (pass == 2 && *flag == 0) {
+        // the first pass sufficed: R = R1, already final in the workspace
+        if (ru_out && (int)threadIdx.x < r) {
+            const double *r1 = (const double *)(wsb + off_r1);
+            float *ru = ru_out + (size_t)b * r * r;
+            for (int i = 0; i < r; ++i)
+                ru[i * r + threadIdx.x] = (float)r1[i * RP + threadIdx.x];
+        }
+        return;
+    }
     __shared__ double G[RP][RP + 1];
     __shared__ double Rs[RP][RP + 1];
     __shared__ double S1[RP][RP + 1];  // pass 2: R1^-1
@@ -1063,6 +1091,7 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
     //    the far end, so x[i + 1], the value just computed, enters last and the
     //    rows' sums overlap.
     double x[RP];
+    double sx = 0.0;  // ||column lane of R^-1||^2, for the condition estimate
 #pragma unroll
     for (int i = RP - 1; i >= 0; --i) {
         double s = 0.0;
@@ -1072,6 +1101,7 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
         // (delta - s) / R[i][i]: below the diagonal every x[k] in s is zero, so
         // one expression covers all three cases without a branch
         x[i] = ((i == lane ? 1.0 : 0.0) - s) * rdiag[i];
+        sx = fma(x[i], x[i], sx);
     }
 
     double *r1 = (double *)(wsb + off_r1), *r1inv = (double *)(wsb + off_r1inv);
@@ -1079,14 +1109,34 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
     if (!col)
         return;
     if (pass == 1) {
+        // R1 and R1^-1; R1^-1 is the final R^-1 unless the second pass runs
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
             r1[i * RP + lane] = Rs[i][lane];
             r1inv[i * RP + lane] = x[i];
+            rinv[i * RP + lane] = x[i];
         }
+        // 4. condition estimate ||R1||_F^2 ||R1^-1||_F^2 (>= kappa_2(M)^2): the
+        //    columns' sums of squares through LDS, then every lane adds them in
+        //    the same order, so that all lanes (and runs) decide alike
+        double sr = 0.0;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            sr = fma(Rs[i][lane], Rs[i][lane], sr);
+        G[0][lane] = sr;  // G is no longer read
+        G[1][lane] = sx;
+        __syncthreads();
+        double tr2 = 0.0, tx2 = 0.0;
+#pragma unroll
+        for (int j = 0; j < RP; ++j) {
+            tr2 += G[0][j];
+            tx2 += G[1][j];
+        }
+        if (lane == 0)  // a NaN estimate takes the second pass
+            *flag = (tr2 * tx2 <= kTwoPassKappa2) ? 0 : 1;
         return;
     }
-    // 4. pass 2: column lane of R2 R1 and of R1^-1 R2^-1, four rows at a time
+    // 5. pass 2: column lane of R2 R1 and of R1^-1 R2^-1, four rows at a time
     //    (their sums interleave), the group's stores after its sums
     float *ru = ru_out ? ru_out + (size_t)b * r * r : nullptr;
     const bool ru_col = ru != nullptr && lane < r;
@@ -1240,16 +1290,18 @@ hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_s
     const unsigned ggrid = (unsigned)(gblocks * batch), agrid = (unsigned)(ablocks * batch);
     hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
                        m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
-                       nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r);
+                       nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r,
+                       Ly.off_flag);
     hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 1, Ly.off_r1, Ly.off_r1inv,
-                       Ly.off_rinv, (float *)nullptr);
+                       Ly.off_rinv, ru, Ly.off_flag);
+    // the second pass: work-groups of matrices whose first pass sufficed return at once
     hipLaunchKernelGGL((lr_gram_kernel<RP, true>), dim3(ggrid), dim3(kThreads), 0, st, M,
                        m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
-                       (float *)nullptr, 1, (int64_t)0);
+                       (float *)nullptr, 1, (int64_t)0, Ly.off_flag);
     hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 2, Ly.off_r1, Ly.off_r1inv,
-                       Ly.off_rinv, ru);
+                       Ly.off_rinv, ru, Ly.off_flag);
     hipLaunchKernelGGL((lr_apply_kernel<RP>), dim3(agrid), dim3(kThreads), 0, st, M, m_stride, L,
                        Lp_ops, r, ws, Ly.layer_bytes, Ly.off_rinv, ops, Ly.off_qops, out,
                        out_stride, ablocks);

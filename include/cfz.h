@@ -183,10 +183,12 @@ size_t cfz_lowrank_workspace_bytes(int64_t batch, int64_t m, int64_t n, int32_t 
 /* Algorithm 3 (Subspace Iteration, rank r) on `batch` independent matrices
  * (paper: reproducibility table, "Pseudocode", Algorithm 3):
  *   Q = orth(Q0); T times { Z = A^T (A Q); Q = orth(Z) }; (U, R_U) = orth(A Q); V = Q.
- * orth() is a thin QR with positive diagonal (Cholesky-QR applied twice, Gram
- * matrix and r x r Cholesky in fp64); a column whose pivot is <= 1e-13 of the
- * mean squared column norm is dropped (zero column of Q, zero row and column
- * of R).  The reconstruction of A is U R_U V^T = (A Q) Q^T.
+ * orth() is a thin QR with positive diagonal: Cholesky-QR with the Gram
+ * matrix and r x r Cholesky in fp64, repeated once (CholQR2) for the matrices
+ * whose condition estimate ||R||_F ||R^-1||_F from the first pass exceeds 2^14.5,
+ * where one pass could lose more orthogonality than fp32 output keeps; a column
+ * whose pivot is <= 1e-13 of the mean squared column norm is dropped (zero
+ * column of Q, zero row and column of R).  The reconstruction of A is U R_U V^T = (A Q) Q^T.
  * A: [batch][m][n] bf16.  Q0: [batch][n][r] fp32 random sample (caller-drawn); it
  * may be the V buffer itself (a warm start from the previous call's V): Q0 is
  * read in full before V is written.

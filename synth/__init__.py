@@ -143,6 +143,19 @@ def lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=0, key="lowrank", devic
     return a.to(torch.bfloat16)
 
 
+def graded_batch(batch, m, n, k=48, decades=4.0, seed=0, key="graded", device="cpu"):
+    """Ill-conditioned inputs: A = F diag(s) G^T with F (m x k), G (n x k) Gaussian and
+    s_i = 10^(-decades * i / (k - 1)), i < k -- a spectrum that falls geometrically over
+    ``decades`` decades -- as bf16 (built in fp64 on the CPU, then moved to ``device``)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(seed, key, batch, m, n, k, int(decades * 1000)))
+    f = torch.randn((batch, m, k), generator=g, dtype=torch.float64)
+    gg = torch.randn((batch, n, k), generator=g, dtype=torch.float64)
+    s = torch.pow(10.0, -decades * torch.arange(k, dtype=torch.float64) / max(k - 1, 1))
+    a = torch.bmm(f * s, gg.transpose(1, 2).contiguous())
+    return a.to(torch.bfloat16).to(device)
+
+
 def exact_rank_batch(batch, m, n, rank, seed=0, key="exact", device="cpu"):
     """A = F G^T with F, G entries in {-1, 0, 1}: every entry is an integer of size <= rank,
     so A is exactly representable in bf16 for rank <= 256 and has rank <= ``rank`` exactly."""
