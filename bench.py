@@ -69,10 +69,22 @@ def load_traffic(kernel, workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(xs_host, bits, group, budget_s=20.0):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
+def host_cpu():
+    """The host's CPU model name and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "cores_available": len(os.sched_getaffinity(0))}
 
+
+def _cpu_codec_rate(xs_host, bits, group, budget_s):
     import oracle
 
     n_tensors = len(xs_host[0])
@@ -91,11 +103,28 @@ def cpu_baseline(xs_host, bits, group, budget_s=20.0):
                 break
         if t_total > budget_s:
             break
-    elems = done * n
-    return {"value": round(2 * elems / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} tensor-steps of 1024x3072 (compress+decode, int{bits} g{group}, "
-                      f"DELTA), single-threaded C oracle, {t_total:.1f} s"}, np
+    return done, t_total, 2 * done * n / t_total / 1e9
+
+
+def cpu_baseline(xs_host, bits, group, budget_s=20.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: its OpenMP
+    build on all the host's cores (same source, bit-identical results), and beside it the
+    single-threaded build."""
+    import oracle
+
+    with oracle.parallel():
+        cores = oracle.threads()
+        done_p, t_p, rate_p = _cpu_codec_rate(xs_host, bits, group, budget_s / 2)
+    done_1, t_1, rate_1 = _cpu_codec_rate(xs_host, bits, group, budget_s)
+    what = f"1024x3072 (compress+decode, int{bits} g{group}, DELTA)"
+    out = {"value": round(rate_p, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done_p} tensor-steps of {what}, C oracle built with OpenMP on {cores} "
+                     f"threads, {t_p:.1f} s",
+           **host_cpu(),
+           "single_core": {"value": round(rate_1, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"{done_1} tensor-steps of {what}, single-threaded C "
+                                     f"oracle, {t_1:.1f} s"}}
+    return out
 
 
 def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps):
@@ -331,6 +360,58 @@ def _ef_modes_one(cfz, torch, X, slots, rows, cols, bits, group, steps):
     return out
 
 
+def bench_error_trajectory(cfz, torch, X, slots, rows, cols, bits=4, group=64):
+    """Receiver error ||X_t - base_t|| / ||X_t|| over all tensors after every compressed step
+    (steps 1 .. slots - 1 of the pre-generated, consecutive AR(1) steps, DELTA, grouped per
+    layer), beside the error of quantizing each X_t directly with the same quantizer (a
+    closed loop from a zero base, re-warmed every step): the residual scheme's gain is their
+    ratio.  The abstract claims temporal redundancy and error feedback that keeps the error
+    from accumulating: the trajectory should stay flat."""
+    T, n = X.shape[1], X.shape[2]
+    dev = X.device
+    prev = torch.empty((T, n), dtype=torch.bfloat16, device=dev)
+    err = torch.empty((T, n), dtype=torch.float32, device=dev)
+    base = torch.empty((T, n), dtype=torch.float32, device=dev)
+    dbase_s = torch.empty((T, n), dtype=torch.float32, device=dev)
+    dbase_r = torch.empty((T, n), dtype=torch.float32, device=dev)
+    codes = torch.empty((T, n * bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, n // group), dtype=torch.float32, device=dev)
+    sd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_SENDER)
+    rd = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_DELTA, cfz.CFZ_RECEIVER)
+    od = cfz.make_desc(rows, cols, bits, group, cfz.CFZ_EF_OFF, cfz.CFZ_SENDER)
+    snd = [cfz.cfz_state_create(sd, prev=prev[i], err=err[i], x0=X[0, i]) for i in range(T)]
+    rcv = [cfz.cfz_state_create(rd, base=base[i], x0=X[0, i]) for i in range(T)]
+    layers = [(2 * l, 2 * l + 1) for l in range(T // 2)]
+    res, direct = [], []
+    for t in range(1, slots):
+        for c in layers:
+            cfz.cfz_compress_group([snd[i] for i in c], [X[t, i] for i in c],
+                                   [codes[i] for i in c], [scales[i] for i in c])
+            cfz.cfz_decompress_group([rcv[i] for i in c], [codes[i] for i in c],
+                                     [scales[i] for i in c])
+        xt = X[t].float()
+        res.append((torch.linalg.vector_norm(base - xt) / torch.linalg.vector_norm(xt)).item())
+        # direct: quantize X_t itself (zero base, re-warmed), decode into a zero base
+        ds = [cfz.cfz_state_create(od, base=dbase_s[i]) for i in range(T)]
+        dr = [cfz.cfz_state_create(rd, base=dbase_r[i]) for i in range(T)]
+        for c in layers:
+            cfz.cfz_compress_group([ds[i] for i in c], [X[t, i] for i in c],
+                                   [codes[i] for i in c], [scales[i] for i in c])
+            cfz.cfz_decompress_group([dr[i] for i in c], [codes[i] for i in c],
+                                     [scales[i] for i in c])
+        direct.append((torch.linalg.vector_norm(dbase_r - xt) / torch.linalg.vector_norm(xt)).item())
+        for h in ds + dr:
+            cfz.cfz_state_destroy(h)
+    for h in snd + rcv:
+        cfz.cfz_state_destroy(h)
+    return {"workload": f"flux-share {T} tensors of {rows}x{cols}, int{bits} g{group}, delta, "
+                        f"steps 1..{slots - 1}",
+            "receiver_rel_error_by_step": [float(f"{e:.4g}") for e in res],
+            "direct_quantization_rel_error_by_step": [float(f"{e:.4g}") for e in direct],
+            "direct_over_residual_error_ratio_last_step": round(direct[-1] / res[-1], 3),
+            "direct_over_residual_error_ratio_min": round(min(d / r for d, r in zip(direct, res)), 3)}
+
+
 def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
     """CogVideoX-2b share at sequence-parallel degree 4: 30 layers x {K, V} of 4388 x 1920
     bf16 (AR(1), alpha 0.97), DELTA, one grouped compress and one grouped decode launch per
@@ -416,7 +497,8 @@ def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
 
 
 def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
-    """The fp64 CPU oracle on one layer per rank; per-call figures scale that by the batch."""
+    """The fp64 CPU oracle on one layer per rank, single-threaded and with OpenMP on all host
+    cores; per-call figures scale the per-layer time by the batch."""
     import numpy as np
 
     import oracle
@@ -424,16 +506,25 @@ def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
 
     a = A_layer.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
     m, n = a.shape
-    res = {"kind": "oracle", "cores": 1, "unit": "ms per call",
-           "sample": f"one {m}x{n} layer per rank, single-threaded fp64 oracle; per-call time "
-                     f"= per-layer time x {batch} (extrapolated)", "per_rank": {}}
+    with oracle.parallel():
+        cores = oracle.threads()
+    res = {"kind": "oracle", "cores": cores, "unit": "ms per call", **host_cpu(),
+           "sample": f"one {m}x{n} layer per rank, fp64 oracle with OpenMP on {cores} threads "
+                     f"and single-threaded; per-call time = per-layer time x {batch} "
+                     "(extrapolated)", "per_rank": {}}
     for r in ranks:
         q0 = gaussian_q0(1, n, r, seed=r)[0].numpy()
+        with oracle.parallel():
+            t0 = time.perf_counter()
+            oracle.lowrank(a, q0, T)
+            dp = time.perf_counter() - t0
         t0 = time.perf_counter()
         oracle.lowrank(a, q0, T)
-        dt = time.perf_counter() - t0
-        res["per_rank"][str(r)] = {"ms_per_layer": round(dt * 1e3, 1),
-                                   "ms_per_call": round(dt * 1e3 * batch, 1)}
+        d1 = time.perf_counter() - t0
+        res["per_rank"][str(r)] = {"ms_per_layer": round(dp * 1e3, 1),
+                                   "ms_per_call": round(dp * 1e3 * batch, 1),
+                                   "single_core_ms_per_layer": round(d1 * 1e3, 1),
+                                   "single_core_ms_per_call": round(d1 * 1e3 * batch, 1)}
     return res
 
 
@@ -675,7 +766,49 @@ def main():
     ce[1].record()
     torch.cuda.synchronize()
     layer_copy_gbs = 3 * 57 * 2 * lay_elems * 2 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
-    del dsts, srcs, gcopy
+    del dsts, gcopy
+    # the same streams at the codec's own read:write ratios (compress 8 : 6.5625, decode
+    # 4.5625 : 4 bytes per element): a large launch, and 57 launches of the per-layer size
+    mix = {}
+    big = src.numel() * 2 // 16 * 16
+    dst_big = torch.empty(big // 2, dtype=torch.bfloat16, device=dev)
+    # compress reads x, prev and err (8 B) and writes the rest; decode reads the payload and
+    # the base and writes the base (4 B)
+    for name, rd, wr in (("compress", 8.0, bc - 8.0), ("decode", bd - 4.0, 4.0)):
+        wbig = int(big * wr / rd) // 16 * 16
+        cfz.cfz_stream_mix(src, big, dst_big, wbig)
+        torch.cuda.synchronize()
+        ce[0].record()
+        for _ in range(3):
+            cfz.cfz_stream_mix(src, big, dst_big, wbig)
+        ce[1].record()
+        torch.cuda.synchronize()
+        big_gbs = 3 * (big + wbig) / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
+        lr_ = int(rd * n * 2) // 16 * 16   # one layer's K and V: 2 n elements
+        lw_ = int(wr * n * 2) // 16 * 16
+        flat_src = srcs.view(-1).view(torch.uint8)
+        msrc = flat_src[: 57 * lr_].view(57, lr_) if flat_src.numel() >= 57 * lr_ else None
+        if msrc is None:
+            msrc = torch.empty((57, lr_), dtype=torch.uint8, device=dev)
+            msrc.view(-1)[: flat_src.numel()].copy_(flat_src[: msrc.numel()])
+        mdst = torch.empty((57, max(lw_, 16)), dtype=torch.uint8, device=dev)
+        gmix = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gmix, stream=cap):
+            for i in range(57):
+                cfz.cfz_stream_mix(msrc[i], lr_, mdst[i], lw_, stream=cap)
+        torch.cuda.synchronize()
+        gmix.replay()
+        torch.cuda.synchronize()
+        ce[0].record()
+        for _ in range(3):
+            gmix.replay()
+        ce[1].record()
+        torch.cuda.synchronize()
+        lay_gbs = 3 * 57 * (lr_ + lw_) / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
+        mix[name] = {"read_to_write": f"{rd:g}:{wr:g}", "large_launch_GB/s": round(big_gbs, 1),
+                     "per_layer_launch_GB/s": round(lay_gbs, 1)}
+        del mdst, gmix
+    del dst_big, srcs
 
     workload = "flux-share-57x2x1024x3072-int4-g64-delta"
     traffic = load_traffic("compress", f"{workload}/{args.launch}")
@@ -719,11 +852,15 @@ def main():
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": bd},
             "stream_copy_ceiling_GB/s": round(copy_gbs, 1),
             "stream_copy_at_compress_launch_size_GB/s": round(layer_copy_gbs, 1),
+            "stream_mix_at_codec_ratios": mix,
         },
         "other_launch_granularities": other_modes,
         "bf16_state": bf16_state,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
     }
+    print("[bench] error trajectory leg", file=sys.stderr, flush=True)
+    line["error_trajectory"] = bench_error_trajectory(cfz, torch, X, slots, rows, cols)
+    torch.cuda.empty_cache()
     if not args.no_ef_modes:
         print("[bench] error-feedback readings leg", file=sys.stderr, flush=True)
         line["ef_modes"] = bench_ef_modes(cfz, torch, X, slots, rows, cols, steps=min(K, 10))
@@ -754,8 +891,7 @@ def main():
         for s in range(min(5, X.shape[0])):
             xh = X[s, :sample_tensors].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             xs_host.append([xh[i] for i in range(sample_tensors)])
-        cb, _ = cpu_baseline(xs_host, bits, group)
-        line["cpu_baseline"] = cb
+        line["cpu_baseline"] = cpu_baseline(xs_host, bits, group)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -74,6 +74,7 @@ def _load():
         "cfz_lowrank_ef_compress": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p], i32),
         "cfz_lowrank_ef_decompress": ([i64, i64, i64, i32, p, p, p, p, p, p], i32),
         "cfz_stream_copy": ([p, p, sz, p], i32),
+        "cfz_stream_mix": ([p, sz, p, sz, p], i32),
         "cfz_status_string": ([i32], C.c_char_p),
         "cfz_last_error": ([], C.c_char_p),
         "cfz_abi_version": ([], C.c_int),
@@ -367,6 +368,15 @@ def cfz_stream_copy(src, dst, nbytes=None, stream=None) -> None:
     _need(src, nbytes, "src")
     _need(dst, nbytes, "dst")
     _check(_lib.cfz_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "cfz_stream_copy")
+
+
+def cfz_stream_mix(src, src_bytes, dst, dst_bytes, stream=None) -> None:
+    """Reads src_bytes of src and writes dst_bytes of dst, the writes spread evenly through
+    the reads (a plain stream with a given read:write ratio)."""
+    _need(src, src_bytes, "src")
+    _need(dst, dst_bytes, "dst")
+    _check(_lib.cfz_stream_mix(_ptr(src), src_bytes, _ptr(dst), dst_bytes, _stream(stream)),
+           "cfz_stream_mix")
 
 
 # ------------------------------------------------------------------ torch-owned state helpers

@@ -609,6 +609,28 @@ cfz_status cfz_lowrank_ef_decompress(int64_t batch, int64_t m, int64_t n, int32_
     return CFZ_OK;
 }
 
+cfz_status cfz_stream_mix(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
+                          void *stream)
+{
+    if (src_bytes == 0)
+        return dst_bytes == 0 ? CFZ_OK : fail(CFZ_ERR_SHAPE, "dst_bytes > src_bytes");
+    if (!src || (dst_bytes && !dst))
+        return fail(CFZ_ERR_NULL, "src and dst are required");
+    if ((src_bytes & 15u) != 0 || (dst_bytes & 15u) != 0)
+        return fail(CFZ_ERR_SHAPE, "byte counts must be multiples of 16");
+    if (dst_bytes > src_bytes)
+        return fail(CFZ_ERR_SHAPE, "dst_bytes > src_bytes");
+    if (src_bytes / 16 > ((size_t)1 << 31))
+        return fail(CFZ_ERR_SHAPE, "src_bytes too large");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(CFZ_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    hipError_t e = cfz::launch_stream_mix(src, dst, (int64_t)(src_bytes / 16),
+                                          (int64_t)(dst_bytes / 16), (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "mixed stream launch");
+    return CFZ_OK;
+}
+
 cfz_status cfz_stream_copy(const void *src, void *dst, size_t bytes, void *stream)
 {
     if (bytes == 0)

@@ -37,6 +37,7 @@ hipError_t launch_decode(const DecodeItem *items, int count, int bits, int group
 hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, void *base, void *err,
                          bool state_bf16, int64_t nchunks, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t nvec, hipStream_t st);
+hipError_t launch_stream_mix(const void *src, void *dst, int64_t nr, int64_t nw, hipStream_t st);
 
 struct LowrankArgs {
     int64_t batch, m, n;

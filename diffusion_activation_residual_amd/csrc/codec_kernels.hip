@@ -420,6 +420,31 @@ cfz_stream_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, i
     }
 }
 
+// Reads nr 16-byte vectors and writes nw <= nr of them: vector i of src goes to
+// dst[i * nw / nr] exactly when that index steps, so the writes are spread evenly
+// through the read stream and the traffic keeps one read:write ratio throughout.
+// One vector per lane, UNROLL per lane, all loads issued before the stores.
+template <int UNROLL>
+__global__ void __launch_bounds__(kBlock)
+cfz_stream_mix_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int64_t nr,
+                      int64_t nw)
+{
+    const int64_t i0 = (int64_t)blockIdx.x * (kBlock * UNROLL) + threadIdx.x;
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = i0 + (int64_t)u * kBlock;
+        v[u] = i < nr ? ld_nt(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = i0 + (int64_t)u * kBlock;
+        const int64_t j = i * nw / nr;
+        if (i < nr && j != (i + 1) * nw / nr)
+            st_nt(v[u], dst + j);
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline unsigned grid_for(int64_t items, int64_t per_block)
@@ -607,6 +632,16 @@ hipError_t launch_warmup(const uint16_t *x0, uint16_t *prev, void *base, void *e
     else
         hipLaunchKernelGGL(cfz_warmup_kernel<false>, dim3(grid_for(nchunks, kBlock)), dim3(kBlock),
                            0, st, x0, prev, base, err, nchunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_mix(const void *src, void *dst, int64_t nr, int64_t nw, hipStream_t st)
+{
+    if (nr == 0)
+        return hipSuccess;
+    constexpr int UNROLL = 4;
+    hipLaunchKernelGGL((cfz_stream_mix_kernel<UNROLL>), dim3(grid_for(nr, kBlock * UNROLL)),
+                       dim3(kBlock), 0, st, (const u32x4 *)src, (u32x4 *)dst, nr, nw);
     return hipGetLastError();
 }
 

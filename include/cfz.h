@@ -277,6 +277,16 @@ cfz_status cfz_lowrank_ef_decompress(int64_t batch, int64_t m, int64_t n, int32_
  * traffic counters and the achievable copy bandwidth.  Not part of the codec. */
 cfz_status cfz_stream_copy(const void *src, void *dst, size_t bytes, void *hip_stream);
 
+/* Measurement aid: reads src_bytes and writes dst_bytes (<= src_bytes; both
+ * multiples of 16, pointers 16-byte aligned, src_bytes <= 2^35): 16-byte
+ * vector i of src is stored to vector floor(i * nw / nr) of dst when that index
+ * steps (nr, nw: the vector counts), so the writes are spread evenly through the
+ * reads.  With the codec's own ratio (compress 8 : 6.5625 bytes per element) it
+ * measures what a plain stream of that read:write mix reaches.  Not part of the
+ * codec. */
+cfz_status cfz_stream_mix(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
+                          void *hip_stream);
+
 const char *cfz_status_string(cfz_status status);
 const char *cfz_last_error(void);
 int cfz_abi_version(void);

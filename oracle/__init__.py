@@ -19,16 +19,19 @@ from . import build as _build
 DELTA, LITERAL, OFF, OPENLOOP = 0, 1, 2, 3
 SENDER, RECEIVER = 0, 1
 
-_lib = None
+_libs = {}            # "serial" / "openmp" -> loaded library
+_active = "serial"
 
 
 def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_build.LIB):
+    """The active build of the oracle: the serial one unless inside ``parallel()``."""
+    lib = _libs.get(_active)
+    if lib is not None:
+        return lib
+    path = _build.LIB_OMP if _active == "openmp" else _build.LIB
+    if not os.path.exists(path):
         _build.build()
-    lib = C.CDLL(_build.LIB)
+    lib = C.CDLL(path)
     p = C.c_void_p
     i64, i32 = C.c_int64, C.c_int
     lib.oracle_pack_codes.argtypes = [i64, i32, p, p]
@@ -47,8 +50,30 @@ def _load():
     lib.oracle_lowrank_ef_decompress.argtypes = [i64, i64, i32, p, p, p, p, p]
     lib.oracle_qmax.argtypes = [i32]
     lib.oracle_qmax.restype = i32
-    _lib = lib
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = i32
+    _libs[_active] = lib
     return lib
+
+
+class parallel:
+    """Within ``with oracle.parallel():`` every call goes to the OpenMP build of the same C
+    source (identical results; used to time the oracle on all host cores)."""
+
+    def __enter__(self):
+        global _active
+        self._prev, _active = _active, "openmp"
+        return self
+
+    def __exit__(self, *exc):
+        global _active
+        _active = self._prev
+        return False
+
+
+def threads() -> int:
+    """Threads the active build's loops use (1 for the serial build)."""
+    return _load().oracle_threads()
 
 
 def _ptr(a):

@@ -90,27 +90,34 @@ int oracle_qmax(int bits) { return (1 << (bits - 1)) - 1; }
 /* ------------------------------------------------------------------ */
 /* Code packing: two's complement b-bit fields, little-endian bit order. */
 
+/* Both loops run over blocks of 8 elements, which fill whole bytes, so that the
+ * blocks are independent (the OpenMP build splits them among threads; the
+ * serial build ignores the pragmas). */
 void oracle_pack_codes(int64_t n, int bits, const int8_t *q, uint8_t *codes)
 {
     int64_t nbytes = n * bits / 8;
     uint8_t mask = (uint8_t)((1u << bits) - 1u);
     memset(codes, 0, (size_t)nbytes);
-    for (int64_t j = 0; j < n; ++j) {
-        int64_t bit = j * bits;
-        codes[bit / 8] |= (uint8_t)(((uint8_t)q[j] & mask) << (bit % 8));
-    }
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < (n + 7) / 8; ++blk)
+        for (int64_t j = 8 * blk; j < 8 * blk + 8 && j < n; ++j) {
+            int64_t bit = j * bits;
+            codes[bit / 8] |= (uint8_t)(((uint8_t)q[j] & mask) << (bit % 8));
+        }
 }
 
 void oracle_unpack_codes(int64_t n, int bits, const uint8_t *codes, int8_t *q)
 {
     uint32_t mask = (1u << bits) - 1u;
-    for (int64_t j = 0; j < n; ++j) {
-        int64_t bit = j * bits;
-        int v = (int)((codes[bit / 8] >> (bit % 8)) & mask);
-        if (v >= (1 << (bits - 1)))       /* sign bit set */
-            v -= (1 << bits);
-        q[j] = (int8_t)v;
-    }
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < (n + 7) / 8; ++blk)
+        for (int64_t j = 8 * blk; j < 8 * blk + 8 && j < n; ++j) {
+            int64_t bit = j * bits;
+            int v = (int)((codes[bit / 8] >> (bit % 8)) & mask);
+            if (v >= (1 << (bits - 1)))       /* sign bit set */
+                v -= (1 << bits);
+            q[j] = (int8_t)v;
+        }
 }
 
 /* ------------------------------------------------------------------ */
@@ -196,8 +203,11 @@ void oracle_compress(int64_t n, int bits, int group, int mode, int state_bf16,
                      uint8_t *codes, float *scales)
 {
     int qmax = oracle_qmax(bits);
-    float *r = (float *)malloc(sizeof(float) * (size_t)group);
     int8_t *q = (int8_t *)malloc((size_t)n);
+#pragma omp parallel
+    {
+    float *r = (float *)malloc(sizeof(float) * (size_t)group);
+#pragma omp for schedule(static)
     for (int64_t g = 0; g < n / group; ++g) {
         int64_t j0 = g * group;
         for (int i = 0; i < group; ++i) {
@@ -225,9 +235,10 @@ void oracle_compress(int64_t n, int bits, int group, int mode, int state_bf16,
                 state_set(base, j, fmaf(qf, s, state_get(base, j, state_bf16)), state_bf16);
         }
     }
+    free(r);
+    }
     oracle_pack_codes(n, bits, q, codes);
     free(q);
-    free(r);
 }
 
 /* One step at the receiver: decode the payload and advance the base.
@@ -237,6 +248,7 @@ void oracle_decompress(int64_t n, int bits, int group, int state_bf16, const uin
 {
     int8_t *q = (int8_t *)malloc((size_t)n);
     oracle_unpack_codes(n, bits, codes, q);
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; ++j) {
         if (q[j] != 0)
             state_set(base, j, fmaf((float)q[j], scales[j / group], state_get(base, j, state_bf16)),
@@ -297,6 +309,7 @@ int oracle_qr(int64_t rows, int cols, const double *M, double *Q, double *R)
             vnorm2 += vi * vi;
         }
         /* apply H = I - 2 v v^T / (v^T v) to columns k..cols-1 */
+#pragma omp parallel for schedule(static)
         for (int j = k; j < cols; ++j) {
             double dot = 0.0;
             for (int64_t i = p; i < rows; ++i)
@@ -320,7 +333,10 @@ int oracle_qr(int64_t rows, int cols, const double *M, double *Q, double *R)
         }
 
     /* Q column k = H_0 H_1 ... H_{nref-1} e_{prow[k]} */
+#pragma omp parallel
+    {
     double *e = (double *)malloc(sizeof(double) * (size_t)rows);
+#pragma omp for schedule(static)
     for (int k = 0; k < cols; ++k) {
         if (prow[k] < 0) {
             for (int64_t i = 0; i < rows; ++i)
@@ -342,6 +358,8 @@ int oracle_qr(int64_t rows, int cols, const double *M, double *Q, double *R)
         for (int64_t i = 0; i < rows; ++i)
             Q[i * cols + k] = e[i];
     }
+    free(e);
+    }
 
     /* sign convention: diag(R) > 0 */
     for (int k = 0; k < cols; ++k) {
@@ -352,7 +370,6 @@ int oracle_qr(int64_t rows, int cols, const double *M, double *Q, double *R)
                 Q[i * cols + k] = -Q[i * cols + k];
         }
     }
-    free(e);
     free(prow);
     free(V);
     free(W);
@@ -365,6 +382,7 @@ int oracle_qr(int64_t rows, int cols, const double *M, double *Q, double *R)
 
 static void mat_AQ(int64_t m, int64_t n, int r, const double *A, const double *Q, double *Y)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int c = 0; c < r; ++c) {
             double acc = 0.0;
@@ -376,6 +394,7 @@ static void mat_AQ(int64_t m, int64_t n, int r, const double *A, const double *Q
 
 static void mat_AtY(int64_t m, int64_t n, int r, const double *A, const double *Y, double *Z)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; ++j)
         for (int c = 0; c < r; ++c) {
             double acc = 0.0;
@@ -488,3 +507,12 @@ void oracle_lowrank_ef_decompress(int64_t m, int64_t n, int r, const double *U, 
 }
 
 int oracle_abi_version(void) { return 2; }
+
+/* Threads the loops above may use: 1 in the serial build, OpenMP's count (all
+ * cores unless OMP_NUM_THREADS says otherwise) in the OpenMP build. */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif

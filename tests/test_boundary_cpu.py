@@ -14,7 +14,7 @@ MISALIGNED = 0x10008
 
 def test_library_exports_every_declared_function():
     names = cfz.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
     assert cfz.cfz_abi_version() == 3
@@ -170,6 +170,19 @@ def test_lowrank_ef_validation():
     assert lib.cfz_lowrank_ef_warmup(16, MISALIGNED, ALIGNED, None, None, None) == \
         cfz.CFZ_ERR_ALIGN
     assert lib.cfz_lowrank_ef_warmup(0, None, ALIGNED, ALIGNED, ALIGNED, None) == cfz.CFZ_OK
+
+
+def test_stream_mix_validation():
+    lib = cfz._lib
+    assert lib.cfz_stream_mix(None, 32, ALIGNED, 16, None) == cfz.CFZ_ERR_NULL
+    assert lib.cfz_stream_mix(ALIGNED, 32, None, 16, None) == cfz.CFZ_ERR_NULL
+    assert lib.cfz_stream_mix(ALIGNED, 32, ALIGNED, 48, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_stream_mix(ALIGNED, 33, ALIGNED, 16, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_stream_mix(ALIGNED, 32, ALIGNED, 17, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_stream_mix(ALIGNED, (1 << 35) + 16, ALIGNED, 16, None) == cfz.CFZ_ERR_SHAPE
+    assert lib.cfz_stream_mix(MISALIGNED, 32, ALIGNED, 16, None) == cfz.CFZ_ERR_ALIGN
+    assert lib.cfz_stream_mix(None, 0, None, 0, None) == cfz.CFZ_OK
+    assert lib.cfz_stream_mix(None, 0, None, 16, None) == cfz.CFZ_ERR_SHAPE
 
 
 def test_stream_copy_validation():

@@ -310,6 +310,24 @@ def test_error_paths_have_no_side_effects():
     assert cfz.cfz_state_steps(s.handle) == 0
 
 
+@pytest.mark.parametrize("nr,nw", [(1000, 1000), (1000, 820), (4096 * 3 + 5, 3001), (64, 1),
+                                   (7, 0)])
+def test_stream_mix_writes_the_spread_vectors(nr, nw):
+    """Vector i of src lands at floor(i nw / nr) of dst when that index steps: every dst
+    vector is written once, by the last src vector that maps to it."""
+    src = torch.randint(0, 2**31 - 1, (nr * 4,), dtype=torch.int32, device=DEV)
+    dst = torch.full((max(nw, 1) * 4 + 4,), -1, dtype=torch.int32, device=DEV)
+    cfz.cfz_stream_mix(src, nr * 16, dst, nw * 16)
+    torch.cuda.synchronize()
+    i = np.arange(nr, dtype=np.int64)
+    j = i * nw // nr
+    last = j != (i + 1) * nw // nr
+    expect = np.full(((max(nw, 1) + 1) * 4,), -1, dtype=np.int32)
+    s = src.cpu().numpy().reshape(nr, 4)
+    expect.reshape(-1, 4)[j[last]] = s[i[last]]
+    assert np.array_equal(dst.cpu().numpy(), expect)
+
+
 def test_stream_copy_matches():
     say("[gpu] stream copy")
     a = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=DEV)
