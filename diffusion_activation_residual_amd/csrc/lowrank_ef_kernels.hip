@@ -153,32 +153,26 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
     // this lane's operands of V R_U^T: row c = col0 + 64 w + 16 ct + li, k = g J + j,
-    // accumulated over l = 0 .. r-1 in order (a partly rolled loop keeps the registers
-    // few and still has 16 loads in flight)
+    // accumulated over l = 0 .. r-1 in order; row c of V read whole with vector loads
     float vop[4][J];
-    const float *vp[4];
-    bool cv[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         const int64_t c = col0 + 64 * wave + 16 * ct + li;
-        cv[ct] = c < n;
-        vp[ct] = Vb + (cv[ct] ? c : 0) * r;
+        float vr[RP];
+        if (c < n)
+            load_floats<RP>(Vb + c * r, r, r == RP, vr);
+        else
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-            vop[ct][j] = 0.0f;
-    }
-#pragma unroll 4
-    for (int l = 0; l < r; ++l) {
-        float v[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-            v[ct] = cv[ct] ? vp[ct][l] : 0.0f;
+            for (int l = 0; l < RP; ++l)
+                vr[l] = 0.0f;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const float rk = sR[g * J + j][l];
+            float acc = 0.0f;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                vop[ct][j] = __builtin_fmaf(v[ct], rk, vop[ct][j]);
+            for (int l = 0; l < RP; ++l)
+                if (l < r)
+                    acc = __builtin_fmaf(vr[l], sR[g * J + j][l], acc);
+            vop[ct][j] = acc;
         }
     }
 
@@ -257,7 +251,11 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
 // Rows per work-group: each work-group first forms its columns' rows of V R_U^T
 // (r x r work per column), so at r = 32 taller blocks amortise that better
 // (1024 rows: 334 / 408 us per sender / receiver call at 57 x 1024 x 3072,
-// against 423 / 493 us with 256); at r <= 16, 256 rows is fastest.
+// against 423 / 493 us with 256); at r <= 16, 256 rows is fastest.  Reading each
+// row of V whole with vector loads (rather than one float of 16 rows per load)
+// took the r = 16 update from 290 to 277 us (367 to 357 with the bf16 output);
+// loading the next 32-row block ahead, or a resident grid walking equal shares of
+// 32 x 256 units, were no faster (the first costs a wave of occupancy).
 template <int RP>
 constexpr int upd_rows() { return RP == 32 ? 4 * kUpdRows : kUpdRows; }
 
