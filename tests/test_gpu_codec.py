@@ -428,6 +428,64 @@ def test_flux_int2_batched_full_size_sampled_rows():
     _batched_rows_parity("flux", 2, 32, SPECS["flux"].steps, sl, "flux int2 batched")
 
 
+def test_flux_int2_batched_whole_batch_first_steps():
+    """All 57 layers' K/V as one 116736 x 3072 tensor, int2 g32, one launch per step: every
+    code, scale and state value of the whole batch compared with the oracle (its OpenMP
+    build, identical bits to the serial one) for compressed steps 1 to 3."""
+    sp = SPECS["flux"]
+    rows = sp.tensors * sp.rows
+    n = rows * sp.cols
+    st = AR1Stream.from_spec(sp, seed=5, device=DEV)
+    say(f"[gpu] flux int2 whole batch: {rows} x {sp.cols}, steps 1-3")
+    x = st.next().reshape(rows, sp.cols)
+    gs = cfz.Sender(rows, sp.cols, 2, 32, x0=x)
+    gr = cfz.Receiver(rows, sp.cols, 2, 32, x0=x)
+    with oracle.parallel():
+        os_ = oracle.Sender(n, 2, 32, oracle.DELTA, x0=u16(x))
+        or_ = oracle.Receiver(n, 2, 32, x0=u16(x))
+    for t in range(1, 4):
+        x = st.next().reshape(rows, sp.cols)
+        codes, scales = gs.compress(x)
+        gr.decompress(codes, scales)
+        torch.cuda.synchronize()
+        with oracle.parallel():
+            oc, osc = os_.compress(u16(x))
+            or_.decompress(oc, osc)
+        _compare_step(f"flux int2 whole batch t{t}", gs, gr, codes, scales, os_, or_, oc, osc)
+    gs.close()
+    gr.close()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_flux_literal_and_off_full_layer_every_step(mode):
+    """The LITERAL and OFF readings at full size: one FLUX.1-dev layer (its K and V, 1024 x
+    3072 each) in the benchmark's grouped per-layer launches, int4 g64, all 27 compressed
+    steps, every value compared with the oracle."""
+    sp = SPECS["flux"]
+    st = AR1Stream(2, sp.rows, sp.cols, sp.alpha, sp.noise, sp.outlier_frac, seed=6 + mode,
+                   key="flux-layer")
+    n = sp.rows * sp.cols
+    say(f"[gpu] flux one layer, mode {mode}, {sp.steps - 1} steps")
+    x = st.next()
+    gs = [cfz.Sender(sp.rows, sp.cols, 4, 64, mode, x0=x[i].to(DEV).contiguous()) for i in (0, 1)]
+    gr = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x[i].to(DEV).contiguous()) for i in (0, 1)]
+    os_ = [oracle.Sender(n, 4, 64, MODE_PAIRS[mode], x0=u16(x[i])) for i in (0, 1)]
+    or_ = [oracle.Receiver(n, 4, 64, x0=u16(x[i])) for i in (0, 1)]
+    for t in range(1, sp.steps):
+        x = st.next()
+        xd = [x[i].to(DEV).contiguous() for i in (0, 1)]
+        cfz.cfz_compress_group([g.handle for g in gs], xd, [g.codes for g in gs],
+                               [g.scales for g in gs])
+        cfz.cfz_decompress_group([g.handle for g in gr], [g.codes for g in gs],
+                                 [g.scales for g in gs])
+        torch.cuda.synchronize()
+        for i in (0, 1):
+            oc, osc = os_[i].compress(u16(x[i]))
+            or_[i].decompress(oc, osc)
+            _compare_step(f"mode {mode} t{t} tensor {i}", gs[i], gr[i], gs[i].codes,
+                          gs[i].scales, os_[i], or_[i], oc, osc)
+
+
 @pytest.mark.parametrize("bits,group", [(4, 64), (2, 32)])
 def test_cogvideox_full_size_sampled_rows(bits, group):
     """CogVideoX-2b share, 30 layers x {K, V} of 4388 x 1920 in one launch per step, 50 steps."""

@@ -282,3 +282,34 @@ def test_non_finite_matrix_leaves_the_others_bitwise():
     dirty = run_gpu(dirty_A, Q0, r, 2)
     for x, y in zip(clean, dirty):
         assert np.array_equal(x[0], y[0])
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_full_batch_every_step_first_and_last_layer(r):
+    """The benchmark's low-rank workload over a whole request: 28 steps, each a fresh batch
+    of 57 matrices of 1024 x 3072 (rank 16 + 0.05 noise) and a fresh Q0, T = 2; layers 0
+    and 56 of every step compared with the oracle (the oracle's OpenMP build, identical
+    bits to the serial one).  At r = 32 the trailing 16 columns span noise and are not
+    compared."""
+    batch, m, n, T, steps = 57, 1024, 3072, 2, 28
+    say(f"[gpu] lowrank full batch r={r}: {steps} steps, layers 0 and 56")
+    U = torch.empty(batch, m, r, device=DEV)
+    V = torch.empty(batch, n, r, device=DEV)
+    RU = torch.empty(batch, r, r, device=DEV)
+    ws = torch.empty(cfz.cfz_lowrank_workspace_bytes(batch, m, n, r), dtype=torch.uint8,
+                     device=DEV)
+    for t in range(steps):
+        A = lowrank_batch(batch, m, n, rank=16, sigma=0.05, seed=1000 * r + t, device=DEV)
+        Q0 = gaussian_q0(batch, n, r, seed=2000 * r + t, device=DEV)
+        cfz.cfz_lowrank(batch, m, n, r, T, A, Q0, U, V, RU, ws)
+        torch.cuda.synchronize()
+        k = min(r, 16)
+        for b in (0, batch - 1):
+            with oracle.parallel():
+                ou, ov, oru = oracle.lowrank(u16(A[b]), Q0[b].cpu().numpy(), T)
+            Ub, Vb, Rb = (x[b].double().cpu().numpy() for x in (U, V, RU))
+            tag = f"step {t} layer {b}"
+            assert rel(Ub @ Rb @ Vb.T, ou @ oru @ ov.T) <= TOL, f"{tag}: reconstruction"
+            assert rel(Ub[:, :k], ou[:, :k]) <= TOL, f"{tag}: U"
+            assert rel(Vb[:, :k], ov[:, :k]) <= TOL, f"{tag}: V"
+            assert rel(Rb[:k, :k], oru[:k, :k]) <= TOL, f"{tag}: R_U"
