@@ -792,6 +792,122 @@ lr_ata8_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint
     }
 }
 
+// P = A Q (fp32 [m][r]) for r <= 16 and n <= 3072, the final product of the
+// iteration, built like the one-pass product's first phase: 16 waves, 16-row panels
+// of A through LDS (wave w loads row w of the next panel into registers while the
+// current one is used), and each wave holding the Q hi and Q lo operands of its
+// 32-column blocks in registers for the whole kernel, so the panels are the only
+// memory loads in the loop.  Per panel each wave multiplies its blocks by Q hi and
+// Q lo into a 16 x 16 partial, and the 16 partials are added in wave order for the
+// panel's rows of P.  No partial sums cross work-groups: each owns whole rows.
+template <int RP>
+__global__ void __launch_bounds__(kAtaThreads)
+lr_aqp_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r,
+              uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_qops, size_t off_out,
+              int64_t np, int splits, int64_t split_rows)
+{
+    static_assert(RP == 16, "Q hi and lo of 16 columns stay in registers");
+    constexpr int kChunks = 6;
+    constexpr int kPanel = 16;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / splits, s = lid % splits;
+    uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    const bf16x8 *qhi = (const bf16x8 *)(wsb + off_qops);
+    const bf16x8 *qlo = qhi + (np / 8) * RP;
+    float *out = (float *)(wsb + off_out);
+
+    const int64_t row0 = (int64_t)s * split_rows;
+    const int64_t rows_here = m - row0 <= 0 ? 0 : (m - row0 < split_rows ? m - row0 : split_rows);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (int64_t)b * m * n + row0 * n, (uint32_t)(rows_here * n * 2));
+
+    __shared__ __attribute__((aligned(16))) uint16_t sp[kPanel * kAtaSrowMax];
+    __shared__ f32x4 sy[kAtaWaves][64];  // each wave's 16 x 16 partial, in its D layout
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
+    const int nb = (int)((n + 31) / 32);
+    const int nbw = (nb + kAtaWaves - 1) / kAtaWaves;
+    const int kb0 = wave * nbw;
+    const int kbn = nb - kb0 < nbw ? nb - kb0 : nbw;
+    const int srow = (int)round_up(32 * nb, 128) + 24;
+    const int cpr = (int)(n / 8);
+
+    // wave w loads row w of a panel: chunk k of a lane is columns 8 (lane + 64 k) .. + 7
+    auto load_panel = [&](int64_t p, u32x4 (&v)[kChunks]) {
+        const uint32_t base = (uint32_t)((p * kPanel + wave) * n * 2);
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+            const int cc = lane + 64 * k;
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, cc < cpr ? base + (uint32_t)cc * 16 : kOOB, 0, 2 /*nt*/);
+        }
+    };
+    auto store_panel = [&](const u32x4 (&v)[kChunks]) {
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+            const int cc = lane + 64 * k;
+            if (cc < cpr)
+                *(u32x4 *)&sp[wave * srow + 8 * cc] = v[k];
+        }
+    };
+
+    u32x4 pf[kChunks];
+    load_panel(0, pf);
+
+    // Q operands of this wave's blocks: slot (4 (kb0 + j) + g, li) of each plane
+    bf16x8 qh[kAtaMaxBlocks], ql[kAtaMaxBlocks];
+#pragma unroll
+    for (int j = 0; j < kAtaMaxBlocks; ++j) {
+        const int64_t slot = (int64_t)(4 * (kb0 + (j < kbn ? j : 0)) + g) * RP + li;
+        qh[j] = j < kbn ? qhi[slot] : bf16x8{};
+        ql[j] = j < kbn ? qlo[slot] : bf16x8{};
+    }
+
+    // columns n .. 32 nb - 1 of every panel row stay zero (they are multiplied)
+    const int tailc = (32 * nb - (int)n) / 8;
+    if ((int)threadIdx.x < kPanel * tailc) {
+        const int row = threadIdx.x / tailc, cc = threadIdx.x % tailc;
+        *(u32x4 *)&sp[row * srow + (int)n + 8 * cc] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const int64_t npanels = (rows_here + kPanel - 1) / kPanel;
+    for (int64_t p = 0; p < npanels; ++p) {
+        store_panel(pf);
+        load_panel(p + 1, pf);  // past the last panel: all out of range, zeros, unused
+        __syncthreads();        // the panel is in LDS (and the previous one's partials read)
+
+        f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kAtaMaxBlocks; ++j) {
+            if (j < kbn) {
+                const bf16x8 a = *(const bf16x8 *)&sp[li * srow + 32 * (kb0 + j) + 8 * g];
+                y = mfma(a, qh[j], y);
+                y = mfma(a, ql[j], y);
+            }
+        }
+        sy[wave][lane] = y;  // D layout: rows 4g..4g+3 of column li
+        __syncthreads();     // every partial written, every wave done with the panel
+        if (threadIdx.x < 64) {
+            // the lane's four values: rows 4g + v, column li, summed over the waves in order
+            f32x4 t = sy[0][threadIdx.x];
+#pragma unroll 3
+            for (int w = 1; w < kAtaWaves; ++w) {
+                const f32x4 u = sy[w][threadIdx.x];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    t[v] += u[v];
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = row0 + p * kPanel + 4 * g + v;
+                if (row < row0 + rows_here && li < r)
+                    out[row * r + li] = t[v];
+            }
+        }
+    }
+}
+
 int ata_splits(int64_t batch, int64_t m, int64_t n, int r)
 {
     if (r > 16 || n > kAtaMaxN || batch <= 0)
@@ -1359,9 +1475,19 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
             return e;
     }
     // final: P = A Q, (U, R_U) = orth(P), V = Q (already written)
-    hipLaunchKernelGGL((lr_aq_kernel<RP, false>), dim3((unsigned)(aq_blocks * a.batch)),
-                       dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes, Ly.off_qops,
-                       Ly.off_mf, Ly.mp, Ly.np, aq_blocks);
+    bool aq_done = false;
+    if constexpr (RP == 16) {
+        if (Ly.splits > 0) {
+            hipLaunchKernelGGL((lr_aqp_kernel<RP>), dim3((unsigned)(Ly.splits * a.batch)),
+                               dim3(kAtaThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
+                               Ly.off_qops, Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows);
+            aq_done = true;
+        }
+    }
+    if (!aq_done)
+        hipLaunchKernelGGL((lr_aq_kernel<RP, false>), dim3((unsigned)(aq_blocks * a.batch)),
+                           dim3(kThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
+                           Ly.off_qops, Ly.off_mf, Ly.mp, Ly.np, aq_blocks);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return run_orth<RP>(Ly, a.batch, mf, mf_stride, a.m, a.r, ws, a.U, a.m * a.r, false, a.RU,
