@@ -497,6 +497,9 @@ static hipError_t compress_g(const CompressItem *it, int count, int64_t total_qu
     if (count == 1)
         return big ? compress_chunk<BITS, G, MODE, SB, 1, 1>(it, 1, st)
                    : compress_chunk<BITS, G, MODE, SB, 4, 1>(it, 1, st);
+    if (count == 2)  // a layer's K and V: a 128-byte table (about 0.2% faster than 1 KB)
+        return big ? compress_chunk<BITS, G, MODE, SB, 1, 2>(it, 2, st)
+                   : compress_chunk<BITS, G, MODE, SB, 4, 2>(it, 2, st);
     return big ? compress_chunk<BITS, G, MODE, SB, 1, kMaxGroup>(it, count, st)
                : compress_chunk<BITS, G, MODE, SB, 4, kMaxGroup>(it, count, st);
 }
@@ -577,6 +580,9 @@ static hipError_t decode_g(const DecodeItem *it, int count, int64_t tq, hipStrea
     if (count == 1)
         return big ? decode_chunk<BITS, G, SB, 1, 1>(it, 1, st)
                    : decode_chunk<BITS, G, SB, 4, 1>(it, 1, st);
+    if (count == 2)
+        return big ? decode_chunk<BITS, G, SB, 1, 2>(it, 2, st)
+                   : decode_chunk<BITS, G, SB, 4, 2>(it, 2, st);
     return big ? decode_chunk<BITS, G, SB, 1, kMaxGroup>(it, count, st)
                : decode_chunk<BITS, G, SB, 4, kMaxGroup>(it, count, st);
 }
