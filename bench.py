@@ -5,13 +5,17 @@ One step = one denoising step of the FLUX.1-dev share at patch degree 4: the
 layer's pair in one grouped compress launch (residual + error feedback + int4
 group-64 quantization + state update, DELTA mode) and one grouped decode launch
 (unpack + base update).  Inputs are seeded AR(1) activations, generated into
-HBM before the timed region; the launches of one step are captured once into
-HIP graphs and replayed.
+HBM before the timed region.  A layer's compress and decode stay in order on
+one stream; the layers are spread round-robin over --streams streams (3 by
+default) so that one layer's launches overlap another's, and the launches of
+one step are captured once into a HIP graph and replayed.
 
 value = bf16 activation bytes coded per second: 2 bytes x elements per step x
 steps / elapsed (compress + decode).  The roofline entry is for the compress
 kernel: algorithmic bytes per launch over its average launch duration, timed
-with HIP events on the stream the kernels run on.
+with HIP events on the stream the kernels run on, in a second timed pass of
+the same launches on one stream (events around the compress and the decode
+phase of each step; overlapped launches have no duration of their own).
 
 Further legs in the same JSON line: other launch granularities (per tensor,
 16 tensors), the three error-feedback readings with their receiver error,
@@ -20,7 +24,7 @@ share, the subspace iteration at r = 8/16/32, the rank-r compressor inside
 error feedback (random or warm-started Q0), and the CPU oracle on a bounded
 sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 27] [--warmup 1] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 27] [--warmup 1] [--streams 3] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -534,6 +538,8 @@ def main():
     ap.add_argument("--steps", type=int, default=27)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=3,
+                    help="streams the per-layer launches are spread over (1 = one stream)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--no-batched", action="store_true", help="skip the one-launch-per-step int2 leg")
     ap.add_argument("--no-lowrank", action="store_true", help="skip the subspace-iteration leg")
@@ -557,7 +563,7 @@ def main():
     import numpy as np
     import torch
 
-    from diffusion_activation_residual_amd import cfz
+    from diffusion_activation_residual_amd import cadence, cfz
     from synth import SPECS, AR1Stream
 
     sp = SPECS["flux"]
@@ -601,10 +607,17 @@ def main():
     # tensors per call: 2 = the K and V of one layer, 1 = each tensor alone, T = the whole step
     per_call = {"layer": 2, "tensor": 1, "step": T}
 
-    def run_mode(mode, K, W, use_graph, sb=False):
+    def run_mode(mode, K, W, use_graph, sb=False, streams=1):
+        """K timed steps after W warm-up steps.  streams == 1: each step is a compress graph
+        then a decode graph on one stream, with HIP events around each phase (per-launch
+        kernel times).  streams > 1 (per-layer launches from graphs only): each step is one
+        graph of the layers spread round-robin over the streams (the overlapped schedule),
+        with events only at step boundaries."""
         g = per_call[mode]
         calls = [list(range(i, min(i + g, T))) for i in range(0, T, g)]
         launches = sum((len(c) + 15) // 16 for c in calls)
+        if streams > 1 and not (mode == "layer" and use_graph):
+            raise ValueError("several streams only for per-layer launches from graphs")
         snd, rcv = fresh_states(sb)
 
         def compress_phase(slot):
@@ -630,15 +643,23 @@ def main():
             graphs = {}
             cap = torch.cuda.Stream()
             cap.wait_stream(torch.cuda.current_stream())
-            gd = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gd, stream=cap):
-                decode_phase()
-            for s_ in range(1, slots):
-                gc = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gc, stream=cap):
-                    compress_phase(s_)
-                graphs[s_] = gc
-            graphs["dec"] = gd
+            if streams > 1:
+                sts = [cap] + [torch.cuda.Stream() for _ in range(streams - 1)]
+                for s_ in range(1, slots):
+                    gs_ = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gs_, stream=cap):
+                        cadence.enqueue_layer_step(calls, snd, rcv, X[s_], codes, scales, sts)
+                    graphs[s_] = gs_
+            else:
+                gd = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gd, stream=cap):
+                    decode_phase()
+                for s_ in range(1, slots):
+                    gc = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gc, stream=cap):
+                        compress_phase(s_)
+                    graphs[s_] = gc
+                graphs["dec"] = gd
             torch.cuda.synchronize()
             for h in snd + rcv:
                 cfz.cfz_state_destroy(h)
@@ -647,6 +668,11 @@ def main():
 
         def run_step(step, ev=None):
             s_ = slot_of(step)
+            if streams > 1:
+                graphs[s_].replay()
+                if ev is not None:
+                    ev.record()
+                return
             if ev is not None:
                 ev[0].record()
             graphs[s_].replay() if graphs else compress_phase(s_)
@@ -659,26 +685,46 @@ def main():
         for step in range(1, W + 1):
             run_step(step)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        if streams > 1:  # one event per step boundary
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        else:
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if streams > 1:
+            evs[0].record()
         for k in range(K):
-            run_step(W + 1 + k, evs[k])
+            run_step(W + 1 + k, evs[k + 1] if streams > 1 else evs[k])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         for h in snd + rcv:
             cfz.cfz_state_destroy(h)
-        t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
-        t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
-        per_step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+        if streams > 1:
+            t_comp = t_dec = None
+            per_step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(K))
+        else:
+            t_comp = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
+            t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+            per_step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
         return {"elapsed": elapsed, "t_comp": t_comp, "t_dec": t_dec, "launches": launches,
                 "tensors_per_launch": T / launches, "per_step_ms": per_step_ms}
 
-    print(f"[bench] timing {K} steps ({args.launch} launches)", file=sys.stderr, flush=True)
-    res = run_mode(args.launch, K, W, not args.no_graph)
-    elapsed, t_comp, t_dec = res["elapsed"], res["t_comp"], res["t_dec"]
+    overlap = args.launch == "layer" and not args.no_graph and args.streams > 1
+    nstreams = args.streams if overlap else 1
+    print(f"[bench] timing {K} steps ({args.launch} launches, {nstreams} stream(s))",
+          file=sys.stderr, flush=True)
+    res = run_mode(args.launch, K, W, not args.no_graph, streams=nstreams)
+    elapsed = res["elapsed"]
+    # per-launch kernel times: the same launches on one stream, events around each phase
+    if overlap:
+        print(f"[bench] timing {K} steps on one stream (per-launch kernel times)",
+              file=sys.stderr, flush=True)
+        kres = run_mode(args.launch, K, W, True, streams=1)
+    else:
+        kres = res
+    t_comp, t_dec = kres["t_comp"], kres["t_dec"]
     bc, bd = algorithmic_bytes(bits, group)
-    n_launch = K * res["launches"]
+    n_launch = K * kres["launches"]
     per_launch_elems = n * T / res["launches"]
     avg_comp = t_comp / n_launch
     avg_dec = t_dec / n_launch
@@ -707,6 +753,7 @@ def main():
         print("[bench] bf16-state leg", file=sys.stderr, flush=True)
         kb = min(K, 10)
         r_ = run_mode(args.launch, kb, 1, not args.no_graph, sb=True)
+        r_ov = run_mode(args.launch, kb, 1, True, sb=True, streams=nstreams) if overlap else r_
         bc16, bd16 = algorithmic_bytes(bits, group, state_bf16=True)
         nl = kb * r_["launches"]
         pe = n * T / r_["launches"]
@@ -718,7 +765,8 @@ def main():
                         "error and base in bf16", "steps": kb,
             "traffic_bytes_per_launch": {"compress": load_traffic("compress_bf16_state", wl16),
                                          "decode": load_traffic("decode_bf16_state", wl16)},
-            "activation_GB/s": round(2 * n * T * kb / r_["elapsed"] / 1e9, 2),
+            "activation_GB/s": round(2 * n * T * kb / r_ov["elapsed"] / 1e9, 2),
+            "activation_GB/s_one_stream": round(2 * n * T * kb / r_["elapsed"] / 1e9, 2),
             "compress": {"avg_launch_us": round(r_["t_comp"] / nl * 1e6, 3),
                          "GB/s": round(c16, 1), "frac_hbm_peak": round(c16 / HBM_PEAK_GBS, 4),
                          "bytes_per_elem": bc16},
@@ -820,7 +868,7 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(elapsed / K * 1e3, 4),
-        "step_ms_events": {  # compress + decode of one step, HIP events on the launch stream
+        "step_ms_events": {  # compress + decode of one step, HIP events at step boundaries
             "median": round(res["per_step_ms"][len(res["per_step_ms"]) // 2], 4),
             "min": round(res["per_step_ms"][0], 4),
             "max": round(res["per_step_ms"][-1], 4)},
@@ -837,8 +885,11 @@ def main():
                    "launch": {"layer": "one grouped compress and decode launch per layer (K and V)",
                               "tensor": "one compress and decode launch per tensor",
                               "step": "grouped launches of 16 tensors over the whole step"}[
-                       args.launch] + (", replayed from HIP graphs" if not args.no_graph else
-                                       ", eager")},
+                       args.launch] + (f", layers round-robin over {nstreams} streams, one HIP "
+                                       "graph per step" if overlap else
+                                       ", replayed from HIP graphs" if not args.no_graph else
+                                       ", eager"),
+                   "streams": nstreams},
         "roofline": {"bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "cfz_compress_kernel<bits=4, G=64, DELTA>",
@@ -854,6 +905,9 @@ def main():
             "stream_copy_at_compress_launch_size_GB/s": round(layer_copy_gbs, 1),
             "stream_mix_at_codec_ratios": mix,
         },
+        "schedules": {  # activation GB/s of the same per-layer launches
+            f"{nstreams}_streams": round(value, 2),
+            "1_stream": round(2 * n * T * K / kres["elapsed"] / 1e9, 2)},
         "other_launch_granularities": other_modes,
         "bf16_state": bf16_state,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),

@@ -389,6 +389,65 @@ def test_flux_int4_full_size_sampled_tensors(state_bf16):
                           os_[j], or_[j], oc, osc)
 
 
+def test_flux_int4_layer_streams_graph_every_step():
+    """The benchmark's overlapped schedule: all 57 layers' K and V of the FLUX.1-dev share
+    (114 tensors of 1024 x 3072), int4 g64, DELTA, each layer's grouped compress and decode on
+    one of 3 streams round-robin, captured into one HIP graph per step and replayed for all 27
+    compressed steps.  Layers 0, 28 and 56 (with the bf16 output) are compared with the oracle
+    every step; every tensor's codes and states are compared at the end with a run of the same
+    launches eagerly on one stream."""
+    from diffusion_activation_residual_amd import cadence
+    sp = SPECS["flux"]
+    T, n = sp.tensors, sp.rows * sp.cols
+    layers = [[2 * l, 2 * l + 1] for l in range(T // 2)]
+    picks = [0, 1, 56, 57, 112, 113]
+    say(f"[gpu] flux int4, 3-stream graph schedule, {sp.steps - 1} steps, tensors {picks}")
+    st = AR1Stream.from_spec(sp, seed=9, device=DEV)
+    x0 = st.next().reshape(T, n)
+    xs = torch.empty((T, n), dtype=torch.bfloat16, device=DEV)  # the graph's input buffer
+    xhat = torch.empty((T, n), dtype=torch.bfloat16, device=DEV)
+    gs = [cfz.Sender(sp.rows, sp.cols, 4, 64, x0=x0[i]) for i in range(T)]
+    gr = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x0[i]) for i in range(T)]
+    es = [cfz.Sender(sp.rows, sp.cols, 4, 64, x0=x0[i]) for i in range(T)]  # one-stream run
+    er = [cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=x0[i]) for i in range(T)]
+    eh = torch.empty((T, n), dtype=torch.bfloat16, device=DEV)
+    os_ = [oracle.Sender(n, 4, 64, oracle.DELTA, x0=u16(x0[i])) for i in picks]
+    or_ = [oracle.Receiver(n, 4, 64, x0=u16(x0[i])) for i in picks]
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    streams = [cap, torch.cuda.Stream(), torch.cuda.Stream()]
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):  # records the launches; runs nothing
+        cadence.enqueue_layer_step(layers, [g.handle for g in gs], [g.handle for g in gr], xs,
+                                   [g.codes for g in gs], [g.scales for g in gs], streams,
+                                   xhat=xhat)
+    torch.cuda.synchronize()
+    one = [torch.cuda.current_stream()]
+    for t in range(1, sp.steps):
+        x = st.next().reshape(T, n)
+        xs.copy_(x)
+        graph.replay()
+        cadence.enqueue_layer_step(layers, [g.handle for g in es], [g.handle for g in er], x,
+                                   [g.codes for g in es], [g.scales for g in es], one, xhat=eh)
+        torch.cuda.synchronize()
+        for j, i in enumerate(picks):
+            oc, osc = os_[j].compress(u16(x[i]))
+            oh = or_[j].decompress(oc, osc, want_xhat=True)
+            _compare_step(f"3-stream graph t{t} tensor {i}", gs[i], gr[i], gs[i].codes,
+                          gs[i].scales, os_[j], or_[j], oc, osc, xhat[i], oh)
+    for i in range(T):
+        assert torch.equal(gs[i].codes, es[i].codes), f"tensor {i} codes"
+        assert torch.equal(gs[i].scales.view(torch.int32), es[i].scales.view(torch.int32))
+        assert torch.equal(gs[i].err.view(torch.int32), es[i].err.view(torch.int32))
+        assert torch.equal(gs[i].prev.view(torch.int16), es[i].prev.view(torch.int16))
+        assert torch.equal(gr[i].base.view(torch.int32), er[i].base.view(torch.int32))
+    assert torch.equal(xhat.view(torch.int16), eh.view(torch.int16))
+    del graph
+    for h in gs + gr + es + er:
+        h.close()
+
+
 def _batched_rows_parity(spec_name, bits, group, steps, row_slices, tag):
     sp = SPECS[spec_name]
     rows = sp.tensors * sp.rows
