@@ -1013,47 +1013,89 @@ lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
     for (int p = 0; p < NP; ++p)
         acc[p] = f64x4{0.0, 0.0, 0.0, 0.0};
     const int64_t w0 = (int64_t)blk * kGramRows + wave * WROWS;
-    for (int tt = 0; tt < WROWS / 16; ++tt) {
-        const int64_t t0 = w0 + 16 * tt;
-        if (t0 >= L)
-            break;  // per wave; no barrier inside this loop
-        f64x4 tile[CT];
-        if constexpr (TRANSFORM) {
-            tile_times_rinv<RP>(Mb, L, r, t0, g, c, rb, tile);
-        } else {
+    if constexpr (!TRANSFORM && RP == 16) {
+        // every element of the wave's rows, x[tt][v] = M[w0 + 16 tt + 4 v + g][c] summed
+        // over the partials: all loads in flight together, and every store (Msum aliases
+        // M) after every load
+        constexpr int NT = WROWS / 16;
+        float x[NT][4], pv[kMaxPartials - 1][NT][4];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = w0 + 16 * tt + 4 * v + g;
+                const bool ok = row < L && c < r;
+                const int64_t o = row * r + c;
+                x[tt][v] = ok ? Mb[o] : 0.0f;
+#pragma unroll
+                for (int q = 1; q < kMaxPartials; ++q)
+                    pv[q - 1][tt][v] = (ok && q < nsum) ? Mb[o + q * pstride] : 0.0f;
+            }
+#pragma unroll
+        for (int q = 1; q < kMaxPartials; ++q)
+            if (q < nsum)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        x[tt][v] += pv[q - 1][tt][v];
+        if (nsum > 1)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int64_t row = t0 + 4 * v + g;
-                    const int col = 16 * ct + c;
-                    float x = 0.0f;
-                    if (row < L && col < r) {
-                        const int64_t o = row * r + col;
-                        x = Mb[o];
-                        if (nsum > 1) {
-                            float pv[kMaxPartials];
-#pragma unroll
-                            for (int q = 1; q < kMaxPartials; ++q)
-                                pv[q] = q < nsum ? Mb[o + q * pstride] : 0.0f;
-#pragma unroll
-                            for (int q = 1; q < kMaxPartials; ++q)
-                                if (q < nsum)
-                                    x += pv[q];
-                            Msum[(int64_t)b * m_stride + o] = x;
-                        }
-                    }
-                    tile[ct][v] = (double)x;
+                    const int64_t row = w0 + 16 * tt + 4 * v + g;
+                    if (row < L && c < r)
+                        Msum[(int64_t)b * m_stride + row * r + c] = x[tt][v];
                 }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[0] = mfma64((double)x[tt][v], (double)x[tt][v], acc[0]);
+    } else {
+        for (int tt = 0; tt < WROWS / 16; ++tt) {
+            const int64_t t0 = w0 + 16 * tt;
+            if (t0 >= L)
+                break;  // per wave; no barrier inside this loop
+            f64x4 tile[CT];
+            if constexpr (TRANSFORM) {
+                tile_times_rinv<RP>(Mb, L, r, t0, g, c, rb, tile);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t row = t0 + 4 * v + g;
+                        const int col = 16 * ct + c;
+                        float x = 0.0f;
+                        if (row < L && col < r) {
+                            const int64_t o = row * r + col;
+                            x = Mb[o];
+                            if (nsum > 1) {
+                                float pv[kMaxPartials];
+#pragma unroll
+                                for (int q = 1; q < kMaxPartials; ++q)
+                                    pv[q] = q < nsum ? Mb[o + q * pstride] : 0.0f;
+#pragma unroll
+                                for (int q = 1; q < kMaxPartials; ++q)
+                                    if (q < nsum)
+                                        x += pv[q];
+                                Msum[(int64_t)b * m_stride + o] = x;
+                            }
+                        }
+                        tile[ct][v] = (double)x;
+                    }
+            }
+            int p = 0;
+#pragma unroll
+            for (int ta = 0; ta < CT; ++ta)
+#pragma unroll
+                for (int tb = ta; tb < CT; ++tb, ++p)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[p] = mfma64(tile[ta][v], tile[tb][v], acc[p]);
         }
-        int p = 0;
-#pragma unroll
-        for (int ta = 0; ta < CT; ++ta)
-#pragma unroll
-            for (int tb = ta; tb < CT; ++tb, ++p)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[p] = mfma64(tile[ta][v], tile[tb][v], acc[p]);
     }
     int p = 0;
 #pragma unroll
@@ -1073,99 +1115,50 @@ lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
 
 // ------------------------------------------------------------------ Cholesky + inverse
 
-// One wavefront per matrix.  Sums the Gram partials in a fixed order, factors
-// G = R^T R (R upper, positive diagonal) in fp64 with lane j holding column j in
-// registers (pivots and multipliers broadcast with readlane), and inverts R by
-// back substitution, again one column per lane.
-// pass 1: store R1 and R1^-1, R1^-1 also as the final R^-1, and decide whether
-// the matrix needs the second pass (flag at off_flag).  pass 2: for a flagged
-// matrix, overwrite the final R^-1 with (R1^-1 R2^-1) and, when ru_out is
-// given, store R = R2 R1 as fp32 [r][r]; for the others only R = R1.
-template <int RP>
-__global__ void __launch_bounds__(kCholThreads)
-lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, int gram_blocks,
-               int r, int pass, size_t off_r1, size_t off_r1inv, size_t off_rinv,
-               float *__restrict__ ru_out, size_t off_flag)
+// Orders one wavefront's LDS accesses (write, then other lanes read) without a
+// work-group barrier: the factorisation below runs on one wave of a larger
+// work-group too.
+__device__ __forceinline__ void wave_sync()
 {
-    const int b = blockIdx.x;
-    uint8_t *wsb = ws + (size_t)b * layer_bytes;
-    int32_t *flag = (int32_t *)(wsb + off_flag);
-    if (pass == 2 && *flag == 0) {
-        // the first pass sufficed: R = R1, already final in the workspace
-        if (ru_out && (int)threadIdx.x < r) {
-            const double *r1 = (const double *)(wsb + off_r1);
-            float *ru = ru_out + (size_t)b * r * r;
-            for (int i = 0; i < r; ++i)
-                ru[i * r + threadIdx.x] = (float)r1[i * RP + threadIdx.x];
-        }
-        return;
-    }
-    __shared__ double G[RP][RP + 1];
-    __shared__ double Rs[RP][RP + 1];
-    __shared__ double S1[RP][RP + 1];  // pass 2: R1^-1
-    __shared__ double rdiag[RP];
-    const int lane = threadIdx.x;
-    constexpr int PER = RP * RP / kCholThreads;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    // 1. sum the partials in a fixed order.  Every load is issued before the
-    //    first add waits: QU partials per round (all the lane's entries of each),
-    //    and in pass 2 R1^-1 alongside.
-    const double *part = (const double *)(wsb + off_gram);
+template <int RP>
+struct CholShared {
+    double G[RP][RP + 1];   // the Gram matrix (entries i <= j are used)
+    double Rs[RP][RP + 1];  // R
+    double S1[RP][RP + 1];  // pass 2: R1^-1
+    double rdiag[RP];
+};
+
+// On one wavefront: factors G = R^T R (R upper, positive diagonal) in fp64 with
+// lane j holding column j in registers (pivots and multipliers broadcast with
+// readlane), stores R in cs.Rs (zero below the diagonal and in dropped and pad
+// columns), and inverts R by back substitution, again one column per lane:
+// x[i] = (R^-1)[i][lane], sx = sum_i x[i]^2.  A pivot <= 1e-13 trace(G) / r, or
+// not finite, drops its column.
+template <int RP>
+__device__ __forceinline__ void chol_factor_invert(CholShared<RP> &cs, int r, int lane,
+                                                   double (&x)[RP], double &sx)
+{
     const bool col = lane < RP;
     const int lc = col ? lane : 0;
-    double s1v[PER];
-    if (pass == 2) {
-        const double *r1inv = (const double *)(wsb + off_r1inv);
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-            s1v[e] = r1inv[lane + kCholThreads * e];
-    }
-    constexpr int QU = PER >= 16 ? 2 : 32 / PER;
-    double sum[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-        sum[e] = 0.0;
-    for (int q0 = 0; q0 < gram_blocks; q0 += QU) {
-        double v[QU][PER];
-#pragma unroll
-        for (int j = 0; j < QU; ++j) {  // past the last partial: re-read it, add nothing
-            const int q = q0 + j < gram_blocks ? q0 + j : gram_blocks - 1;
-#pragma unroll
-            for (int e = 0; e < PER; ++e)
-                v[j][e] = part[(size_t)q * RP * RP + lane + kCholThreads * e];
-        }
-#pragma unroll
-        for (int j = 0; j < QU; ++j)
-#pragma unroll
-            for (int e = 0; e < PER; ++e)
-                sum[e] += q0 + j < gram_blocks ? v[j][e] : 0.0;
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int idx = lane + kCholThreads * e;
-        G[idx / RP][idx % RP] = sum[e];
-    }
-    if (pass == 2)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = lane + kCholThreads * e;
-            S1[idx / RP][idx % RP] = s1v[e];
-        }
-    __syncthreads();
     double tr = 0.0;
 #pragma unroll
     for (int k = 0; k < RP; ++k)
-        tr += k < r ? G[k][k] : 0.0;
+        tr += k < r ? cs.G[k][k] : 0.0;
     const double tol = 1e-13 * tr / r;
 
-    // 2. factorisation: gc[i] = G[i][lane] for i <= lane, overwritten by R[i][lane].
-    //    Steps k >= r only see zero padding; they run with a zero pivot and change nothing.
+    // gc[i] = G[i][lane] for i <= lane, overwritten by R[i][lane].  Steps k >= r
+    // only see zero padding; they run with a zero pivot and change nothing.
     uint32_t dead = 0;
     {
         double gc[RP];
 #pragma unroll
         for (int i = 0; i < RP; ++i)
-            gc[i] = (col && i <= lane) ? G[i][lc] : 0.0;
+            gc[i] = (col && i <= lane) ? cs.G[i][lc] : 0.0;
 #pragma unroll
         for (int k = 0; k < RP; ++k) {
             const double dkk = readlane_f64(gc[k], k);
@@ -1196,60 +1189,148 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
 #pragma unroll
         for (int i = 0; i < RP; ++i)
             if (col)
-                Rs[i][lc] = (zero_col || i > lane) ? 0.0 : gc[i];
+                cs.Rs[i][lc] = (zero_col || i > lane) ? 0.0 : gc[i];
     }
-    __syncthreads();
+    wave_sync();
     if (col)
-        rdiag[lc] = ((dead >> lc) & 1u) ? 0.0 : 1.0 / Rs[lc][lc];
-    __syncthreads();
+        cs.rdiag[lc] = ((dead >> lc) & 1u) ? 0.0 : 1.0 / cs.Rs[lc][lc];
+    wave_sync();
 
-    // 3. inverse: x[i] = (R^-1)[i][lane], bottom row first.  Each sum runs from
-    //    the far end, so x[i + 1], the value just computed, enters last and the
-    //    rows' sums overlap.
-    double x[RP];
-    double sx = 0.0;  // ||column lane of R^-1||^2, for the condition estimate
+    // x[i] = (R^-1)[i][lane], bottom row first.  Each sum runs from the far end,
+    // so x[i + 1], the value just computed, enters last and the rows' sums overlap.
+    sx = 0.0;
 #pragma unroll
     for (int i = RP - 1; i >= 0; --i) {
         double s = 0.0;
 #pragma unroll
         for (int k = RP - 1; k > i; --k)
-            s = fma(Rs[i][k], x[k], s);
+            s = fma(cs.Rs[i][k], x[k], s);
         // (delta - s) / R[i][i]: below the diagonal every x[k] in s is zero, so
         // one expression covers all three cases without a branch
-        x[i] = ((i == lane ? 1.0 : 0.0) - s) * rdiag[i];
+        x[i] = ((i == lane ? 1.0 : 0.0) - s) * cs.rdiag[i];
         sx = fma(x[i], x[i], sx);
     }
+}
+
+// On the same wavefront after a first-pass factorisation: whether the matrix
+// needs the second pass.  Condition estimate ||R1||_F^2 ||R1^-1||_F^2
+// (>= kappa_2(M)^2) from the columns' sums of squares, added through LDS in the
+// same order by every lane so that all lanes (and runs) decide alike; a NaN
+// estimate takes the second pass.  Overwrites rows 0 and 1 of cs.G.
+template <int RP>
+__device__ __forceinline__ bool chol_needs_second_pass(CholShared<RP> &cs, int lane, double sx)
+{
+    if (lane < RP) {
+        double sr = 0.0;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            sr = fma(cs.Rs[i][lane], cs.Rs[i][lane], sr);
+        cs.G[0][lane] = sr;
+        cs.G[1][lane] = sx;
+    }
+    wave_sync();
+    double tr2 = 0.0, tx2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+        tr2 += cs.G[0][j];
+        tx2 += cs.G[1][j];
+    }
+    return !(tr2 * tx2 <= kTwoPassKappa2);
+}
+
+// One wavefront per matrix.  Sums the Gram partials in a fixed order, then the
+// factorisation and inverse above.
+// pass 1: store R1 and R1^-1, R1^-1 also as the final R^-1, and decide whether
+// the matrix needs the second pass (flag at off_flag).  pass 2: for a flagged
+// matrix, overwrite the final R^-1 with (R1^-1 R2^-1) and, when ru_out is
+// given, store R = R2 R1 as fp32 [r][r]; for the others only R = R1.
+template <int RP>
+__global__ void __launch_bounds__(kCholThreads)
+lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, int gram_blocks,
+               int r, int pass, size_t off_r1, size_t off_r1inv, size_t off_rinv,
+               float *__restrict__ ru_out, size_t off_flag)
+{
+    const int b = blockIdx.x;
+    uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    int32_t *flag = (int32_t *)(wsb + off_flag);
+    if (pass == 2 && *flag == 0) {
+        // the first pass sufficed: R = R1, already final in the workspace
+        if (ru_out && (int)threadIdx.x < r) {
+            const double *r1 = (const double *)(wsb + off_r1);
+            float *ru = ru_out + (size_t)b * r * r;
+            for (int i = 0; i < r; ++i)
+                ru[i * r + threadIdx.x] = (float)r1[i * RP + threadIdx.x];
+        }
+        return;
+    }
+    __shared__ CholShared<RP> cs;
+    const int lane = threadIdx.x;
+    constexpr int PER = RP * RP / kCholThreads;
+
+    // 1. sum the partials in a fixed order.  Every load is issued before the
+    //    first add waits: QU partials per round (all the lane's entries of each),
+    //    and in pass 2 R1^-1 alongside.
+    const double *part = (const double *)(wsb + off_gram);
+    double s1v[PER];
+    if (pass == 2) {
+        const double *r1inv = (const double *)(wsb + off_r1inv);
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            s1v[e] = r1inv[lane + kCholThreads * e];
+    }
+    constexpr int QU = PER >= 16 ? 2 : 32 / PER;
+    double sum[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        sum[e] = 0.0;
+    for (int q0 = 0; q0 < gram_blocks; q0 += QU) {
+        double v[QU][PER];
+#pragma unroll
+        for (int j = 0; j < QU; ++j) {  // past the last partial: re-read it, add nothing
+            const int q = q0 + j < gram_blocks ? q0 + j : gram_blocks - 1;
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                v[j][e] = part[(size_t)q * RP * RP + lane + kCholThreads * e];
+        }
+#pragma unroll
+        for (int j = 0; j < QU; ++j)
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                sum[e] += q0 + j < gram_blocks ? v[j][e] : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = lane + kCholThreads * e;
+        cs.G[idx / RP][idx % RP] = sum[e];
+    }
+    if (pass == 2)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + kCholThreads * e;
+            cs.S1[idx / RP][idx % RP] = s1v[e];
+        }
+    wave_sync();
+
+    // 2.-3. factorisation and inverse
+    double x[RP], sx;
+    chol_factor_invert<RP>(cs, r, lane, x, sx);
 
     double *r1 = (double *)(wsb + off_r1), *r1inv = (double *)(wsb + off_r1inv);
     double *rinv = (double *)(wsb + off_rinv);
-    if (!col)
+    if (lane >= RP)
         return;
     if (pass == 1) {
         // R1 and R1^-1; R1^-1 is the final R^-1 unless the second pass runs
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
-            r1[i * RP + lane] = Rs[i][lane];
+            r1[i * RP + lane] = cs.Rs[i][lane];
             r1inv[i * RP + lane] = x[i];
             rinv[i * RP + lane] = x[i];
         }
-        // 4. condition estimate ||R1||_F^2 ||R1^-1||_F^2 (>= kappa_2(M)^2): the
-        //    columns' sums of squares through LDS, then every lane adds them in
-        //    the same order, so that all lanes (and runs) decide alike
-        double sr = 0.0;
-#pragma unroll
-        for (int i = 0; i < RP; ++i)
-            sr = fma(Rs[i][lane], Rs[i][lane], sr);
-        G[0][lane] = sr;  // G is no longer read
-        G[1][lane] = sx;
-        __syncthreads();
-        double tr2 = 0.0, tx2 = 0.0;
-#pragma unroll
-        for (int j = 0; j < RP; ++j) {
-            tr2 += G[0][j];
-            tx2 += G[1][j];
-        }
-        if (lane == 0)  // a NaN estimate takes the second pass
-            *flag = (tr2 * tx2 <= kTwoPassKappa2) ? 0 : 1;
+        // 4. whether the second pass runs
+        const bool two = chol_needs_second_pass<RP>(cs, lane, sx);
+        if (lane == 0)
+            *flag = two ? 1 : 0;
         return;
     }
     // 5. pass 2: column lane of R2 R1 and of R1^-1 R2^-1, four rows at a time
@@ -1271,8 +1352,8 @@ lr_chol_kernel(uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_gram, in
             si[ii] = 0.0;
 #pragma unroll
             for (int k = i; k < RP; ++k) {
-                sw[ii] = fma(Rs[i][k], r1c[k], sw[ii]);
-                si[ii] = fma(S1[i][k], x[k], si[ii]);
+                sw[ii] = fma(cs.Rs[i][k], r1c[k], sw[ii]);
+                si[ii] = fma(cs.S1[i][k], x[k], si[ii]);
             }
         }
 #pragma unroll
@@ -1359,6 +1440,292 @@ lr_apply_kernel(const float *M, int64_t m_stride, int64_t L, int64_t Lp, int r,
     }
 }
 
+// ------------------------------------------------------------------ factor and apply
+
+// Second half of the orthogonalisation for RP = 16 in one launch, after the
+// Gram kernel: each work-group takes kCaRows rows of one matrix and
+//   1. while its apply tiles load, wave 0 adds up the Gram partials in a fixed
+//      order and factors them (the Cholesky, inverse and condition estimate
+//      above) -- every work-group of the matrix repeats this small step, so
+//      that no launch or cross-work-group wait separates it from the apply;
+//   2. only for a matrix the estimate flags: G2 = (M R1^-1)^T (M R1^-1) over
+//      all rows of the matrix, again in every work-group, and wave 0 factors
+//      G2 and forms R1^-1 R2^-1 and R2 R1;
+//   3. Q = M R^-1 on its rows, written as fp32 rows (out) and in the operand
+//      layout (ops); the matrix's first work-group writes R as fp32 (ru_out).
+// This replaces the launches of the first factorisation, of the gated second
+// pass (Gram and factorisation, which matrices whose first pass suffices leave
+// at once) and of the apply.  M's tiles are read with the rows in the low lane
+// bits (the fp64 MFMA's A operand); the D layout result goes through LDS for
+// the row-major and operand-layout stores.  out must not overlap M: the second
+// pass of one work-group reads rows that another may already be writing.
+constexpr int kCaWaves = 4;
+constexpr int kCaThreads = 64 * kCaWaves;
+constexpr int kCaRows = 768;                          // apply rows per work-group
+constexpr int kCaTiles = kCaRows / 16 / kCaWaves;    // 16-row tiles per wave
+constexpr int kCaPass2Tiles = 8;                      // tiles in flight in the second pass
+constexpr int kCaGroup = 4;                           // tiles per LDS round trip of the apply
+
+// A operands (rows in the low lane bits) of NT 16-row tiles from row t0 on, one
+// 16-byte load per lane and tile: av[u][ks] = M[t0 + 16 u + c][4 g + ks], zero
+// past row L or column r.  The MFMA's k index k' = g of chunk ks then stands for
+// column 4 k' + ks; the B operand uses the same assignment (R^-1[4 g + ks][c]).
+template <int NT>
+__device__ __forceinline__ void load_a_tiles(__amdgpu_buffer_rsrc_t rs, int64_t L, int r, int64_t t0,
+                                             int g, int c, float (&av)[NT][4])
+{
+    const bool vec = r % 4 == 0;  // rows of whole 16-byte pieces: one 16-byte load per lane
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int64_t row = t0 + 16 * u + c;
+        if (vec) {
+            const uint32_t off = (row < L && 4 * g < r) ? (uint32_t)((row * r + 4 * g) * 4) : kOOB;
+            // cast as a whole: subscripting the builtin's integer vector result
+            // compiles into one dword load splat over the four elements
+            const f32x4 v =
+                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                av[u][ks] = v[ks];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int k = 4 * g + ks;
+                const uint32_t off = (k < r && row < L) ? (uint32_t)((row * r + k) * 4) : kOOB;
+                av[u][ks] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+            }
+        }
+    }
+}
+
+template <int RP>
+__global__ void __launch_bounds__(kCaThreads)
+lr_cholapply_kernel(const float *M, int64_t m_stride, int64_t L, int r, uint8_t *__restrict__ ws,
+                    size_t layer_bytes, size_t off_gram, int gram_blocks, size_t off_ops,
+                    int64_t Lp_ops, bool ops, float *out, int64_t out_stride,
+                    float *__restrict__ ru_out, int blocks_per_mat)
+{
+    static_assert(RP == 16, "one 16 x 16 fp64 tile per product");
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / blocks_per_mat, blk = lid % blocks_per_mat;
+    const float *Mb = M + (int64_t)b * m_stride;
+    uint8_t *wsb = ws + (size_t)b * layer_bytes;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, g = lane >> 4, c = lane & 15;
+    const int64_t Lp = round_up(L, 64);
+    const int64_t w0 = (int64_t)blk * kCaRows + wave * (kCaRows / kCaWaves);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Mb, (uint32_t)(L * r * 4));
+
+    __shared__ double sg[kCaWaves][RP * RP];
+    __shared__ float sq[kCaWaves][16 * kCaGroup][RP + 1];
+    __shared__ CholShared<RP> cs;
+    __shared__ double r1s[RP][RP + 1];   // R1
+    __shared__ double rfin[RP][RP + 1];  // the final R^-1
+    __shared__ int two_s;
+
+    // 1. the Gram partials in order, then the first factorisation, on wave 0.
+    //    Every wave's apply tiles load meanwhile; wave 0 issues its own after the
+    //    partials, since a wave's loads return in issue order.
+    float av[kCaTiles][4];
+    if (wave != 0)
+        load_a_tiles<kCaTiles>(rs, L, r, w0, g, c, av);
+    if (wave == 0) {
+        const double *part = (const double *)(wsb + off_gram);
+        constexpr int PER = RP * RP / 64;
+        constexpr int QU = 16;  // partials whose loads are in flight together
+        double sum[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            sum[e] = 0.0;
+        for (int q0 = 0; q0 < gram_blocks; q0 += QU) {
+            double v[QU][PER];
+#pragma unroll
+            for (int j = 0; j < QU; ++j)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    v[j][e] = q0 + j < gram_blocks
+                                  ? part[(size_t)(q0 + j) * RP * RP + lane + 64 * e] : 0.0;
+#pragma unroll
+            for (int j = 0; j < QU; ++j)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    if (q0 + j < gram_blocks)
+                        sum[e] += v[j][e];
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + 64 * e;
+            cs.G[idx / RP][idx % RP] = sum[e];
+        }
+        wave_sync();
+        __builtin_amdgcn_sched_barrier(0);  // the partials' loads stay ahead of the tiles'
+        load_a_tiles<kCaTiles>(rs, L, r, w0, g, c, av);
+        double x[RP], sx;
+        chol_factor_invert<RP>(cs, r, lane, x, sx);
+        if (lane < RP) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) {
+                r1s[i][lane] = cs.Rs[i][lane];
+                cs.S1[i][lane] = x[i];
+                rfin[i][lane] = x[i];
+            }
+            const bool two = chol_needs_second_pass<RP>(cs, lane, sx);
+            if (lane == 0)
+                two_s = two ? 1 : 0;
+        }
+    }
+    __syncthreads();
+
+    float *ru = (ru_out && blk == 0) ? ru_out + (size_t)b * r * r : nullptr;
+    // 2. the second pass, for a flagged matrix only: G2 over all rows of the matrix
+    if (two_s != 0) {
+        double rb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            rb[ks] = cs.S1[4 * g + ks][c];
+        f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+        const int64_t ntile = Lp / 16;
+        for (int64_t t0 = (int64_t)wave * kCaPass2Tiles; t0 < ntile; t0 += (int64_t)kCaWaves * kCaPass2Tiles) {
+            float pv[kCaPass2Tiles][4];
+            load_a_tiles<kCaPass2Tiles>(rs, L, r, 16 * t0, g, c, pv);
+#pragma unroll
+            for (int u = 0; u < kCaPass2Tiles; ++u) {
+                f64x4 w = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    w = mfma64((double)pv[u][ks], rb[ks], w);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[u % 2] = mfma64(w[v], w[v], acc[u % 2]);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sg[wave][(4 * v + g) * RP + c] = acc[0][v] + acc[1][v];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < RP * RP / 64; ++e) {
+                const int idx = lane + 64 * e;
+                double t = sg[0][idx];
+#pragma unroll
+                for (int w = 1; w < kCaWaves; ++w)
+                    t += sg[w][idx];
+                cs.G[idx / RP][idx % RP] = t;
+            }
+            wave_sync();
+            double x[RP], sx;
+            chol_factor_invert<RP>(cs, r, lane, x, sx);
+            if (lane < RP) {
+                // column lane of R2 R1 and of R1^-1 R2^-1, four rows at a time (their
+                // sums interleave), the group's stores after its sums
+                const bool ru_col = ru != nullptr && lane < r;
+                double r1c[RP];
+#pragma unroll
+                for (int k = 0; k < RP; ++k)
+                    r1c[k] = r1s[k][lane];
+                constexpr int IG = 4;
+#pragma unroll
+                for (int i0 = 0; i0 < RP; i0 += IG) {
+                    double sw[IG], si[IG];
+#pragma unroll
+                    for (int ii = 0; ii < IG; ++ii) {
+                        const int i = i0 + ii;
+                        sw[ii] = 0.0;
+                        si[ii] = 0.0;
+#pragma unroll
+                        for (int k = i; k < RP; ++k) {
+                            sw[ii] = fma(cs.Rs[i][k], r1c[k], sw[ii]);
+                            si[ii] = fma(cs.S1[i][k], x[k], si[ii]);
+                        }
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < IG; ++ii)
+                        rfin[i0 + ii][lane] = si[ii];
+                    if (ru_col)
+#pragma unroll
+                        for (int ii = 0; ii < IG; ++ii)
+                            if (i0 + ii < r)
+                                ru[(i0 + ii) * r + lane] = (float)sw[ii];
+                }
+            }
+        }
+    } else if (wave == 0 && ru && lane < r) {  // R = R1
+        for (int i = 0; i < r; ++i)
+            ru[i * r + lane] = (float)r1s[i][lane];
+    }
+    __syncthreads();
+
+    // 3. Q = M R^-1 on this work-group's rows
+    double rb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        rb[ks] = rfin[4 * g + ks][c];
+    float *ob = out ? out + (int64_t)b * out_stride : nullptr;
+    bf16x8 *hi = (bf16x8 *)(wsb + off_ops);
+    bf16x8 *lo = hi + (Lp_ops / 8) * RP;
+    static_assert(kCaTiles % kCaGroup == 0, "whole groups of tiles");
+#pragma unroll
+    for (int u0 = 0; u0 < kCaTiles; u0 += kCaGroup) {
+        const int64_t g0 = w0 + 16 * u0;  // first row of the group
+        if (g0 >= Lp)
+            break;  // per wave; only wave-local LDS below
+        f64x4 q[kCaGroup];
+#pragma unroll
+        for (int u = 0; u < kCaGroup; ++u) {
+            q[u] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                q[u] = mfma64((double)av[u0 + u][ks], rb[ks], q[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kCaGroup; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                sq[wave][16 * u + 4 * v + g][c] = (float)q[u][v];
+        wave_sync();
+        if (ob) {  // 4 lanes per row, 4 consecutive columns each
+            const int i = lane >> 2, c0 = (lane & 3) * 4;
+#pragma unroll
+            for (int u = 0; u < kCaGroup; ++u) {
+                const int64_t row = g0 + 16 * u + i;
+                const float *qs = &sq[wave][16 * u + i][c0];
+                if (row < L) {
+                    if (r % 4 == 0) {
+                        if (c0 < r)
+                            *(float4 *)&ob[row * r + c0] = make_float4(qs[0], qs[1], qs[2], qs[3]);
+                    } else
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc)
+                            if (c0 + cc < r)
+                                ob[row * r + c0 + cc] = qs[cc];
+                }
+            }
+        }
+        if (ops) {  // one operand slot (8 rows of one column) per lane and half group
+            const int kb = lane / RP, cc = lane % RP;  // kb 0..3: 8-row blocks of 32 rows
+#pragma unroll
+            for (int h2 = 0; h2 < kCaGroup / 2; ++h2) {
+                const int rr = 32 * h2 + 8 * kb;  // first row of the slot in the group
+                if (g0 + rr < Lp) {
+                    bf16x8 h, l;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float qv = sq[wave][rr + i][cc];
+                        h[i] = (__bf16)qv;
+                        l[i] = (__bf16)(qv - (float)h[i]);
+                    }
+                    const int64_t slot = ((g0 + rr) >> 3) * RP + cc;
+                    hi[slot] = h;
+                    lo[slot] = l;
+                }
+            }
+        }
+        wave_sync();
+    }
+}
+
 // ------------------------------------------------------------------ operand layout
 
 // M (fp32 [L][r]) into the operand layout of A Q: one thread per slot (8 rows of
@@ -1400,14 +1767,28 @@ hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_s
                     int r, uint8_t *ws, float *out, int64_t out_stride, bool ops, float *ru,
                     hipStream_t st, int nsum = 1)
 {
-    const int gblocks = (int)((L + kGramRows - 1) / kGramRows);
     const int64_t Lp_ops = round_up(L, 64);
+    const int gblocks = (int)((L + kGramRows - 1) / kGramRows);
     const int ablocks = (int)((Lp_ops + kApplyRows - 1) / kApplyRows);
     const unsigned ggrid = (unsigned)(gblocks * batch), agrid = (unsigned)(ablocks * batch);
     hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
                        m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
                        nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r,
                        Ly.off_flag);
+    // factorisations and apply in one launch, unless out overlaps M (Q0 passed as V)
+    const char *m0 = (const char *)M, *m1 = (const char *)(M + (batch - 1) * m_stride + L * r);
+    const char *o0 = (const char *)out, *o1 = out ? (const char *)(out + (batch - 1) * out_stride + L * r) : o0;
+    const bool overlap = out != nullptr && o0 < m1 && m0 < o1;
+    if constexpr (RP == 16) {
+        if (!overlap) {
+            const int cblocks = (int)((Lp_ops + kCaRows - 1) / kCaRows);
+            hipLaunchKernelGGL((lr_cholapply_kernel<RP>), dim3((unsigned)(cblocks * batch)),
+                               dim3(kCaThreads), 0, st, M, m_stride, L, r, ws, Ly.layer_bytes,
+                               Ly.off_gram, gblocks, Ly.off_qops, Lp_ops, ops, out, out_stride,
+                               ru, cblocks);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((lr_chol_kernel<RP>), dim3((unsigned)batch), dim3(kCholThreads), 0, st, ws,
                        Ly.layer_bytes, Ly.off_gram, gblocks, r, 1, Ly.off_r1, Ly.off_r1inv,
                        Ly.off_rinv, ru, Ly.off_flag);
