@@ -47,6 +47,7 @@ constexpr int kGramRows = 256;    // rows of M per Gram work-group (64 per wave)
 constexpr int kApplyRows = 256;   // rows of M per apply work-group (64 per wave)
 constexpr int kCholThreads = 64;  // the r x r factorisation runs on one wavefront
 constexpr int kMaxPartials = 8;   // partial sums of Z the Gram kernel adds up
+constexpr int kGramHalf = 2;      // 16-row tiles per wave whose loads are in flight together
 // Second Cholesky-QR pass when ||R1||_F^2 ||R1^-1||_F^2 exceeds 2^29: the first
 // pass's loss of orthogonality, about kappa^2 u_fp64 = kappa^2 2^-53, could then
 // exceed the fp32 output's own rounding, 2^-24.
@@ -1014,45 +1015,59 @@ lr_gram_kernel(const float *M, int64_t m_stride, int64_t L, int r,
         acc[p] = f64x4{0.0, 0.0, 0.0, 0.0};
     const int64_t w0 = (int64_t)blk * kGramRows + wave * WROWS;
     if constexpr (!TRANSFORM && RP == 16) {
-        // every element of the wave's rows, x[tt][v] = M[w0 + 16 tt + 4 v + g][c] summed
-        // over the partials: all loads in flight together, and every store (Msum aliases
-        // M) after every load
-        constexpr int NT = WROWS / 16;
-        float x[NT][4], pv[kMaxPartials - 1][NT][4];
+        // the wave's rows in two halves of kGramHalf 16-row tiles; per half, every element
+        // x[tt][v] = M[t0 + 16 tt + 4 v + g][c] summed over the partials with all loads
+        // in flight together, and every store (Msum aliases M) after every load.  Raw
+        // buffer loads: one 32-bit offset per element, the partial's in a scalar
+        // register; an element past the matrix gets an offset past the end and reads 0.
+        constexpr int NH = kGramHalf;
+        static_assert(WROWS == 2 * 16 * NH, "two halves per wave");
+        const __amdgpu_buffer_rsrc_t rsm =
+            make_rsrc(Mb, (uint32_t)((nsum > 1 ? nsum * pstride : L * r) * 4));
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+        for (int h = 0; h < 2; ++h) {
+            const int64_t t0 = w0 + 16 * NH * h;
+            float x[NH][4], pv[kMaxPartials - 1][NH][4];
+            uint32_t off[NH][4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t row = w0 + 16 * tt + 4 * v + g;
-                const bool ok = row < L && c < r;
-                const int64_t o = row * r + c;
-                x[tt][v] = ok ? Mb[o] : 0.0f;
-#pragma unroll
-                for (int q = 1; q < kMaxPartials; ++q)
-                    pv[q - 1][tt][v] = (ok && q < nsum) ? Mb[o + q * pstride] : 0.0f;
-            }
-#pragma unroll
-        for (int q = 1; q < kMaxPartials; ++q)
-            if (q < nsum)
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        x[tt][v] += pv[q - 1][tt][v];
-        if (nsum > 1)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
+            for (int tt = 0; tt < NH; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int64_t row = w0 + 16 * tt + 4 * v + g;
-                    if (row < L && c < r)
-                        Msum[(int64_t)b * m_stride + row * r + c] = x[tt][v];
+                    const int64_t row = t0 + 16 * tt + 4 * v + g;
+                    off[tt][v] = (row < L && c < r) ? (uint32_t)((row * r + c) * 4) : kOOB;
+                    x[tt][v] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rsm, off[tt][v], 0, 0));
+#pragma unroll
+                    for (int q = 1; q < kMaxPartials; ++q)
+                        pv[q - 1][tt][v] =
+                            q < nsum ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                    rsm, off[tt][v], (int)(q * pstride * 4), 0))
+                                     : 0.0f;
                 }
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+            for (int q = 1; q < kMaxPartials; ++q)
+                if (q < nsum)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                acc[0] = mfma64((double)x[tt][v], (double)x[tt][v], acc[0]);
+                    for (int tt = 0; tt < NH; ++tt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            x[tt][v] += pv[q - 1][tt][v];
+            if (nsum > 1) {
+                const __amdgpu_buffer_rsrc_t rso =
+                    make_rsrc(Msum + (int64_t)b * m_stride, (uint32_t)(L * r * 4));
+#pragma unroll
+                for (int tt = 0; tt < NH; ++tt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x[tt][v]),
+                                                              rso, off[tt][v], 0, 0);
+            }
+#pragma unroll
+            for (int tt = 0; tt < NH; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[0] = mfma64((double)x[tt][v], (double)x[tt][v], acc[0]);
+        }
     } else {
         for (int tt = 0; tt < WROWS / 16; ++tt) {
             const int64_t t0 = w0 + 16 * tt;
