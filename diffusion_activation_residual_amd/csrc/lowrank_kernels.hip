@@ -71,6 +71,25 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ fp64 MFMA helpers
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f64_16x16x4_f64: A[i][k] at lane i + 16 k, B[k][j] at lane j + 16 k,
+// D[i][j] at lane j + 16 (i % 4), item i / 4.
+__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c)
+{
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // ------------------------------------------------------------------ workspace layout
 
 struct Layout {
@@ -103,6 +122,8 @@ Layout make_layout(int64_t batch, int64_t m, int64_t n, int r)
     L.gram_blocks = (lmax + kGramRows - 1) / kGramRows;
     L.splits = ata_splits(batch, m, n, r);
     L.split_rows = L.splits ? round_up((m + L.splits - 1) / L.splits, 16) : 0;
+    if (L.gram_blocks < L.splits)  // the final A Q leaves one Gram partial per row range
+        L.gram_blocks = L.splits;
     // Z or P in fp32 [L][r]; with the one-pass product, Z's partial sums side by side
     const int64_t mf_rows = L.splits * n > lmax ? L.splits * n : lmax;
     size_t off = 0;
@@ -807,7 +828,7 @@ template <int RP>
 __global__ void __launch_bounds__(kAtaThreads)
 lr_aqp_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r,
               uint8_t *__restrict__ ws, size_t layer_bytes, size_t off_qops, size_t off_out,
-              int64_t np, int splits, int64_t split_rows)
+              int64_t np, int splits, int64_t split_rows, size_t off_gram)
 {
     static_assert(RP == 16, "Q hi and lo of 16 columns stay in registers");
     constexpr int kChunks = 6;
@@ -874,6 +895,9 @@ lr_aqp_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r,
         *(u32x4 *)&sp[row * srow + (int)n + 8 * cc] = u32x4{0u, 0u, 0u, 0u};
     }
 
+    // wave 0: this work-group's part of G = P^T P, from the panel's rows of P as it
+    // writes them (rows past m are zero and add nothing)
+    f64x4 gacc = f64x4{0.0, 0.0, 0.0, 0.0};
     const int64_t npanels = (rows_here + kPanel - 1) / kPanel;
     for (int64_t p = 0; p < npanels; ++p) {
         store_panel(pf);
@@ -907,7 +931,18 @@ lr_aqp_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r,
                 if (row < row0 + rows_here && li < r)
                     out[row * r + li] = t[v];
             }
+            // A[i][k] = P[row k][i] and B[k][j] = P[row k][j] at lane (i or j, k): the
+            // lane's value of row 4 k + v
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                gacc = mfma64((double)t[v], (double)t[v], gacc);
         }
+    }
+    if (threadIdx.x < 64) {  // the partial in the Gram kernel's layout: G[i][j] at i RP + j
+        double *part = (double *)(wsb + off_gram) + (size_t)s * RP * RP;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            part[(4 * v + g) * RP + li] = gacc[v];
     }
 }
 
@@ -919,25 +954,6 @@ int ata_splits(int64_t batch, int64_t m, int64_t n, int r)
     s = s < 1 ? 1 : (s > kAtaMaxSplits ? kAtaMaxSplits : s);
     const int64_t panels = (m + kAtaPanel - 1) / kAtaPanel;
     return (int)(s < panels ? s : panels);
-}
-
-// ------------------------------------------------------------------ fp64 MFMA helpers
-
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-// v_mfma_f64_16x16x4_f64: A[i][k] at lane i + 16 k, B[k][j] at lane j + 16 k,
-// D[i][j] at lane j + 16 (i % 4), item i / 4.
-__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c)
-{
-    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ double readlane_f64(double v, int l)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Loads the B operands of M Rinv for every k step and column tile (Rinv upper
@@ -1779,30 +1795,35 @@ lr_ops_kernel(const float *__restrict__ M, int64_t m_stride, int64_t L, int64_t 
 
 // nsum > 1: M (in the workspace) holds nsum partial sums of the matrix, L * r
 // floats apart; the first Gram kernel adds them up in place.
+// pre_gram > 0: the Gram partials of M (pre_gram of them) are already in the
+// workspace; only the r <= 16 path without overlap takes them.
 template <int RP>
 hipError_t run_orth(const Layout &Ly, int64_t batch, const float *M, int64_t m_stride, int64_t L,
                     int r, uint8_t *ws, float *out, int64_t out_stride, bool ops, float *ru,
-                    hipStream_t st, int nsum = 1)
+                    hipStream_t st, int nsum = 1, int pre_gram = 0)
 {
     const int64_t Lp_ops = round_up(L, 64);
     const int gblocks = (int)((L + kGramRows - 1) / kGramRows);
     const int ablocks = (int)((Lp_ops + kApplyRows - 1) / kApplyRows);
     const unsigned ggrid = (unsigned)(gblocks * batch), agrid = (unsigned)(ablocks * batch);
-    hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
-                       m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
-                       nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r,
-                       Ly.off_flag);
     // factorisations and apply in one launch, unless out overlaps M (Q0 passed as V)
     const char *m0 = (const char *)M, *m1 = (const char *)(M + (batch - 1) * m_stride + L * r);
     const char *o0 = (const char *)out, *o1 = out ? (const char *)(out + (batch - 1) * out_stride + L * r) : o0;
     const bool overlap = out != nullptr && o0 < m1 && m0 < o1;
+    if (pre_gram > 0 && (RP != 16 || overlap))
+        return hipErrorInvalidValue;
+    if (pre_gram == 0)
+        hipLaunchKernelGGL((lr_gram_kernel<RP, false>), dim3(ggrid), dim3(kThreads), 0, st, M,
+                           m_stride, L, r, ws, Ly.layer_bytes, Ly.off_r1inv, Ly.off_gram, gblocks,
+                           nsum > 1 ? const_cast<float *>(M) : (float *)nullptr, nsum, L * r,
+                           Ly.off_flag);
     if constexpr (RP == 16) {
         if (!overlap) {
             const int cblocks = (int)((Lp_ops + kCaRows - 1) / kCaRows);
             hipLaunchKernelGGL((lr_cholapply_kernel<RP>), dim3((unsigned)(cblocks * batch)),
                                dim3(kCaThreads), 0, st, M, m_stride, L, r, ws, Ly.layer_bytes,
-                               Ly.off_gram, gblocks, Ly.off_qops, Lp_ops, ops, out, out_stride,
-                               ru, cblocks);
+                               Ly.off_gram, pre_gram > 0 ? pre_gram : gblocks, Ly.off_qops,
+                               Lp_ops, ops, out, out_stride, ru, cblocks);
             return hipGetLastError();
         }
     }
@@ -1878,7 +1899,8 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
         if (Ly.splits > 0) {
             hipLaunchKernelGGL((lr_aqp_kernel<RP>), dim3((unsigned)(Ly.splits * a.batch)),
                                dim3(kAtaThreads), 0, st, a.A, a.m, a.n, a.r, ws, Ly.layer_bytes,
-                               Ly.off_qops, Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows);
+                               Ly.off_qops, Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows,
+                               Ly.off_gram);
             aq_done = true;
         }
     }
@@ -1888,8 +1910,9 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
                            Ly.off_qops, Ly.off_mf, Ly.mp, Ly.np, aq_blocks);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
+    // after lr_aqp_kernel the Gram partials of P (one per row range) are in the workspace
     return run_orth<RP>(Ly, a.batch, mf, mf_stride, a.m, a.r, ws, a.U, a.m * a.r, false, a.RU,
-                        st);
+                        st, 1, aq_done ? Ly.splits : 0);
 }
 
 }  // namespace
