@@ -19,9 +19,9 @@
 // fp32 orthogonality: its loss of orthogonality is about kappa(M)^2 u_fp64, so
 // the second pass is taken when the estimate ||R1||_F ||R1^-1||_F >= kappa(M)
 // exceeds 2^14.5 (kappa^2 u_fp64 > u_fp32).  For r <= 16 this is two launches
-// (Gram partials, then factorisations and apply in lr_cholapply_kernel); for
-// r > 16 five, the second pass's two leaving at once for the matrices that do
-// not need it.  A pivot <= 1e-13 * trace(G) / r (or not finite) drops the
+// (Gram partials, then factorisations and apply in lr_cholapply_kernel; for P
+// the final A Q leaves the Gram partials, so one); for r > 16 five, the second
+// pass's two leaving at once for the matrices that do not need it.  A pivot <= 1e-13 * trace(G) / r (or not finite) drops the
 // column: zero Q column, zero R row and column.
 //
 // Skinny operands live in the workspace in "operand layout": hi and lo bf16
