@@ -234,8 +234,8 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
     Q0 = [gaussian_q0(batch, n, r, seed=s, device=dev) for s in range(steps + 1)]
     xhat = torch.empty(batch * m * n, dtype=torch.bfloat16, device=dev)
 
-    def run(T_, warm, timed):
-        snd = cfz.LowrankSender(batch, m, n, r, x0=X[0])
+    def run(T_, warm, timed, deferred=False):
+        snd = cfz.LowrankSender(batch, m, n, r, x0=X[0], deferred=deferred)
         rcv = cfz.LowrankReceiver(batch, m, n, r, x0=X[0])
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 1)]
         for k in range(steps + 1):  # the first step is an untimed warm-up
@@ -245,6 +245,7 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
             ev[k][1].record()
             rcv.decompress(snd.U, snd.V, snd.RU, xhat)
             ev[k][2].record()
+        snd.flush()
         torch.cuda.synchronize()
         tc = sum(e[0].elapsed_time(e[1]) for e in ev[1:]) / 1e3 / steps
         td = sum(e[1].elapsed_time(e[2]) for e in ev[1:]) / 1e3 / steps
@@ -254,6 +255,7 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
         return tc, td, rel
 
     tc, td, rel = run(T, False, True)
+    tcd, tdd, reld = run(T, False, True, deferred=True)
     accuracy = {}
     for T_, warm in ((1, False), (2, False), (1, True), (2, True)):
         c, _, e = run(T_, warm, False)
@@ -269,6 +271,12 @@ def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps
             "compress_ms": round(tc * 1e3, 4), "decompress_ms": round(td * 1e3, 4),
             "receiver_rel_error_last_step": float(f"{rel:.4g}"),
             "compression_ratio_vs_bf16": round(2 * elems / payload, 1),
+            "deferred_sender": {
+                "note": "each step's error update applied inside the next step's residual pass "
+                        "(bit-identical factors and states)",
+                "activation_GB/s": round(2 * elems / (tcd + tdd) / 1e9, 2),
+                "compress_ms": round(tcd * 1e3, 4),
+                "receiver_rel_error_last_step": float(f"{reld:.4g}")},
             "decompress_update_kernel": {
                 "GB/s": round(upd_bytes / td / 1e9, 1),
                 "frac_hbm_peak": round(upd_bytes / td / 1e9 / HBM_PEAK_GBS, 4),

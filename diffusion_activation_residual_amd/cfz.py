@@ -72,6 +72,9 @@ def _load():
         "cfz_lowrank_ef_workspace_bytes": ([i64, i64, i64, i32], sz),
         "cfz_lowrank_ef_warmup": ([i64, p, p, p, p, p], i32),
         "cfz_lowrank_ef_compress": ([i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p], i32),
+        "cfz_lowrank_ef_compress_deferred": ([i64, i64, i64, i32, i32, i32, p, p, p, p, p, p, p,
+                                              p, sz, p], i32),
+        "cfz_lowrank_ef_flush": ([i64, i64, i64, i32, p, p, p, p, p], i32),
         "cfz_lowrank_ef_decompress": ([i64, i64, i64, i32, p, p, p, p, p, p], i32),
         "cfz_stream_copy": ([p, p, sz, p], i32),
         "cfz_stream_mix": ([p, sz, p, sz, p], i32),
@@ -351,6 +354,33 @@ def cfz_lowrank_ef_compress(batch, m, n, r, T, x, prev, err, Q0, U, V, RU, works
                                         ws_bytes, _stream(stream)), "cfz_lowrank_ef_compress")
 
 
+def cfz_lowrank_ef_compress_deferred(batch, m, n, r, T, pending, x, prev, err, Q0, U, V, RU,
+                                     workspace, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check_lowrank(batch, m, n, r, None, Q0, U, V, RU)
+    c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need_dtype(err, _F32, "err")
+    _need(x, 2 * c, "x")
+    _need(prev, 2 * c, "prev")
+    _need(err, 4 * c, "err")
+    _need(workspace, ws_bytes, "workspace")
+    _check(_lib.cfz_lowrank_ef_compress_deferred(batch, m, n, r, T, int(pending), _bf16_ptr(x),
+                                                 _bf16_ptr(prev), _ptr(err), _ptr(Q0), _ptr(U),
+                                                 _ptr(V), _ptr(RU), _ptr(workspace), ws_bytes,
+                                                 _stream(stream)),
+           "cfz_lowrank_ef_compress_deferred")
+
+
+def cfz_lowrank_ef_flush(batch, m, n, r, U, V, RU, err, stream=None) -> None:
+    _check_lowrank(batch, m, n, r, None, None, U, V, RU)
+    c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
+    _need_dtype(err, _F32, "err")
+    _need(err, 4 * c, "err")
+    _check(_lib.cfz_lowrank_ef_flush(batch, m, n, r, _ptr(U), _ptr(V), _ptr(RU), _ptr(err),
+                                     _stream(stream)), "cfz_lowrank_ef_flush")
+
+
 def cfz_lowrank_ef_decompress(batch, m, n, r, U, V, RU, base, xhat=None, stream=None) -> None:
     _check_lowrank(batch, m, n, r, None, None, U, V, RU)
     c = max(int(batch), 0) * max(int(m), 0) * max(int(n), 0)
@@ -449,10 +479,15 @@ class Receiver:
 
 class LowrankSender:
     """Sender of the rank-r compressor inside error feedback, for ``batch`` tensors of m x n:
-    prev (bf16), err (fp32), the workspace and the payload (U, V, RU) in torch tensors."""
+    prev (bf16), err (fp32), the workspace and the payload (U, V, RU) in torch tensors.
 
-    def __init__(self, batch, m, n, r, x0=None, device="cuda", stream=None):
+    deferred=True: each step leaves its error update pending and the next step applies it inside
+    its residual pass (same results, one pass over err fewer per step); err holds the carried
+    error only after ``flush()``."""
+
+    def __init__(self, batch, m, n, r, x0=None, device="cuda", stream=None, deferred=False):
         self.batch, self.m, self.n, self.r = batch, m, n, r
+        self.deferred, self.pending = deferred, False
         count = batch * m * n
         self.prev = torch.empty(count, dtype=torch.bfloat16, device=device)
         self.err = torch.empty(count, dtype=torch.float32, device=device)
@@ -468,9 +503,22 @@ class LowrankSender:
         return self.ws[: self.batch * self.m * self.n * 2].view(torch.bfloat16)
 
     def compress(self, x, Q0, T, stream=None):
-        cfz_lowrank_ef_compress(self.batch, self.m, self.n, self.r, T, x, self.prev, self.err, Q0,
-                                self.U, self.V, self.RU, self.ws, stream=stream)
+        if self.deferred:
+            cfz_lowrank_ef_compress_deferred(self.batch, self.m, self.n, self.r, T, self.pending,
+                                             x, self.prev, self.err, Q0, self.U, self.V, self.RU,
+                                             self.ws, stream=stream)
+            self.pending = True
+        else:
+            cfz_lowrank_ef_compress(self.batch, self.m, self.n, self.r, T, x, self.prev, self.err,
+                                    Q0, self.U, self.V, self.RU, self.ws, stream=stream)
         return self.U, self.V, self.RU
+
+    def flush(self, stream=None):
+        """Applies a pending update, so that err holds the carried error."""
+        if self.pending:
+            cfz_lowrank_ef_flush(self.batch, self.m, self.n, self.r, self.U, self.V, self.RU,
+                                 self.err, stream)
+            self.pending = False
 
 
 class LowrankReceiver:

@@ -550,10 +550,16 @@ cfz_status cfz_lowrank_ef_warmup(int64_t count, const uint16_t *x0, uint16_t *pr
     return CFZ_OK;
 }
 
-cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
-                                   const uint16_t *x, uint16_t *prev, float *err, const float *Q0,
-                                   float *U, float *V, float *RU, void *ws, size_t ws_bytes,
-                                   void *stream)
+namespace {
+
+// The sender's three forms: kPlain updates err at the end of the call; kDeferred leaves the
+// residual in err; kDeferredPending also first applies the previous deferred call's update
+// (with the factors still in U, V, RU) inside the residual pass.
+enum EfSend { kPlain, kDeferred, kDeferredPending };
+
+cfz_status ef_send(EfSend mode, int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                   const uint16_t *x, uint16_t *prev, float *err, const float *Q0, float *U,
+                   float *V, float *RU, void *ws, size_t ws_bytes, void *stream)
 {
     cfz_status st = check_lowrank_ef_shape(batch, m, n, r);
     if (st != CFZ_OK)
@@ -576,14 +582,60 @@ cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t 
         return fail(CFZ_ERR_ALIGN, "workspace must be 256-byte aligned");
     hipStream_t hs = (hipStream_t)stream;
     uint16_t *A = (uint16_t *)ws;
-    hipError_t e = cfz::launch_lowrank_ef_residual(x, prev, err, A, batch * m * n, hs);
+    hipError_t e = mode == kDeferredPending
+                       ? cfz::launch_lowrank_ef_residual_update(batch, m, n, r, U, V, RU, x, prev,
+                                                                err, A, hs)
+                       : cfz::launch_lowrank_ef_residual(x, prev, err, A, batch * m * n, hs);
     if (e != hipSuccess)
         return hip_fail(e, "residual launch");
     cfz::LowrankArgs a{batch, m, n, r, T, A, Q0, U, V, RU, (uint8_t *)ws + a_bytes};
     e = cfz::launch_lowrank(a, hs);
     if (e != hipSuccess)
         return hip_fail(e, "low-rank launch");
-    e = cfz::launch_lowrank_ef_update(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, hs);
+    if (mode == kPlain) {
+        e = cfz::launch_lowrank_ef_update(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, hs);
+        if (e != hipSuccess)
+            return hip_fail(e, "update launch");
+    }
+    return CFZ_OK;
+}
+
+}  // namespace
+
+cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t r, int32_t T,
+                                   const uint16_t *x, uint16_t *prev, float *err, const float *Q0,
+                                   float *U, float *V, float *RU, void *ws, size_t ws_bytes,
+                                   void *stream)
+{
+    return ef_send(kPlain, batch, m, n, r, T, x, prev, err, Q0, U, V, RU, ws, ws_bytes, stream);
+}
+
+cfz_status cfz_lowrank_ef_compress_deferred(int64_t batch, int64_t m, int64_t n, int32_t r,
+                                            int32_t T, int32_t pending, const uint16_t *x,
+                                            uint16_t *prev, float *err, const float *Q0, float *U,
+                                            float *V, float *RU, void *ws, size_t ws_bytes,
+                                            void *stream)
+{
+    if (pending != 0 && pending != 1)
+        return fail(CFZ_ERR_SHAPE, "pending = %d must be 0 or 1", pending);
+    return ef_send(pending ? kDeferredPending : kDeferred, batch, m, n, r, T, x, prev, err, Q0, U,
+                   V, RU, ws, ws_bytes, stream);
+}
+
+cfz_status cfz_lowrank_ef_flush(int64_t batch, int64_t m, int64_t n, int32_t r, const float *U,
+                                const float *V, const float *RU, float *err, void *stream)
+{
+    cfz_status st = check_lowrank_ef_shape(batch, m, n, r);
+    if (st != CFZ_OK)
+        return st;
+    if (batch == 0)
+        return CFZ_OK;
+    if (!U || !V || !RU || !err)
+        return fail(CFZ_ERR_NULL, "U, V, RU and err are required");
+    if (!aligned16(U) || !aligned16(V) || !aligned16(RU) || !aligned16(err))
+        return fail(CFZ_ERR_ALIGN, "every buffer must be 16-byte aligned");
+    hipError_t e = cfz::launch_lowrank_ef_update(batch, m, n, r, U, V, RU, -1.0f, err, nullptr,
+                                                 (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "update launch");
     return CFZ_OK;

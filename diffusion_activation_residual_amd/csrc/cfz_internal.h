@@ -56,6 +56,12 @@ hipError_t launch_lowrank_ef_residual(const uint16_t *x, uint16_t *prev, float *
 hipError_t launch_lowrank_ef_update(int64_t batch, int64_t m, int64_t n, int r, const float *U,
                                     const float *V, const float *RU, float sign, float *Y,
                                     uint16_t *xhat, hipStream_t st);
+// the sender's pending update e = r0 - (U R_U) V^T fused into the next residual pass:
+// err (holding r0) becomes (x - prev) + e, prev becomes x, A bf16 of the new residual
+hipError_t launch_lowrank_ef_residual_update(int64_t batch, int64_t m, int64_t n, int r,
+                                             const float *U, const float *V, const float *RU,
+                                             const uint16_t *x, uint16_t *prev, float *err,
+                                             uint16_t *A, hipStream_t st);
 int64_t lowrank_ef_update_blocks(int64_t batch, int64_t m, int64_t n);
 
 }  // namespace cfz

@@ -123,12 +123,18 @@ __device__ __forceinline__ void load_floats(const float *p, int valid, bool vec,
 // a time.  The MFMA result holds 16 rows x 4 columns per lane group, so each lane would
 // touch 64-byte pieces of 16 rows; instead the wave passes its 32 x 64 result through
 // its own LDS region and reads and writes Y as 4 rows x 256 bytes per instruction.
-template <int RP, int ROWS>
+// RESID: the sender's pending update fused into the next step's residual pass -- Y is
+// the carried error's buffer holding the previous residual r0; each element becomes
+// e = r0 - D (the value the update alone would store), then the new residual
+// r = (x - prev) + e is stored into Y, x into prev and bf16(r) into A (x, prev and A
+// as in the residual kernel; sign and xhat unused).
+template <int RP, int ROWS, bool RESID>
 __global__ void __launch_bounds__(kThreads)
 lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                     const float *__restrict__ V, const float *__restrict__ RU, float sign,
                     float *__restrict__ Y, uint16_t *__restrict__ xhat, int row_groups,
-                    int col_groups)
+                    int col_groups, const uint16_t *__restrict__ x, uint16_t *__restrict__ prev,
+                    uint16_t *__restrict__ A)
 {
     constexpr int J = RP / 4;
     constexpr int SD = 64 + 4;  // padded row of a wave's result tile (floats)
@@ -188,14 +194,20 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
         if (row0 + 16 * rb >= m)
             break;  // uniform over the work-group
         f32x4 yv[2][4];
+        u32x2 xv[2][4], pv[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int64_t row = row0 + 16 * (rb + h) + 4 * k + g;
-                yv[h][k] = (col_ok && row < m)
-                               ? __builtin_nontemporal_load((const f32x4 *)(Yb + row * n + col))
-                               : f32x4{0, 0, 0, 0};
+                const bool ok = col_ok && row < m;
+                yv[h][k] = ok ? __builtin_nontemporal_load((const f32x4 *)(Yb + row * n + col))
+                              : f32x4{0, 0, 0, 0};
+                if constexpr (RESID) {
+                    const int64_t o = b * m * n + row * n + col;
+                    xv[h][k] = ok ? __builtin_nontemporal_load((const u32x2 *)(x + o)) : u32x2{0, 0};
+                    pv[h][k] = ok ? __builtin_nontemporal_load((const u32x2 *)(prev + o)) : u32x2{0, 0};
+                }
             }
         float uop[2][J];
 #pragma unroll
@@ -232,14 +244,33 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                 if (!col_ok || row >= m)
                     continue;
                 f32x4 o;
+                if constexpr (RESID) {
+                    // e = r0 - D exactly as the sender's update stores it, then the residual
+                    // exactly as the residual kernel forms it
+                    f32x4 ev;
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    o[v] = sign > 0.0f ? yv[h][k][v] + d[v] : yv[h][k][v] - d[v];
-                __builtin_nontemporal_store(o, (f32x4 *)(Yb + row * n + col));
-                if (Xb)
-                    __builtin_nontemporal_store(
-                        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
-                        (u32x2 *)(Xb + row * n + col));
+                    for (int v = 0; v < 4; ++v)
+                        ev[v] = yv[h][k][v] - d[v];
+                    const u32x2 xq = xv[h][k], pq = pv[h][k];
+                    o[0] = (bf16_lo(xq[0]) - bf16_lo(pq[0])) + ev[0];
+                    o[1] = (bf16_hi(xq[0]) - bf16_hi(pq[0])) + ev[1];
+                    o[2] = (bf16_lo(xq[1]) - bf16_lo(pq[1])) + ev[2];
+                    o[3] = (bf16_hi(xq[1]) - bf16_hi(pq[1])) + ev[3];
+                    const int64_t oo = b * m * n + row * n + col;
+                    __builtin_nontemporal_store(o, (f32x4 *)(Yb + row * n + col));
+                    __builtin_nontemporal_store(xq, (u32x2 *)(prev + oo));
+                    // A is read again at once by the subspace iteration: a normal store
+                    *(u32x2 *)(A + oo) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        o[v] = sign > 0.0f ? yv[h][k][v] + d[v] : yv[h][k][v] - d[v];
+                    __builtin_nontemporal_store(o, (f32x4 *)(Yb + row * n + col));
+                    if (Xb)
+                        __builtin_nontemporal_store(
+                            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
+                            (u32x2 *)(Xb + row * n + col));
+                }
             }
         // the next block's writes to the tile come after these reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -261,14 +292,21 @@ constexpr int upd_rows() { return RP == 32 ? 4 * kUpdRows : kUpdRows; }
 
 template <int RP>
 hipError_t update_rp(int64_t batch, int64_t m, int64_t n, int r, const float *U, const float *V,
-                     const float *RU, float sign, float *Y, uint16_t *xhat, hipStream_t st)
+                     const float *RU, float sign, float *Y, uint16_t *xhat, const uint16_t *x,
+                     uint16_t *prev, uint16_t *A, hipStream_t st)
 {
     constexpr int ROWS = upd_rows<RP>();
     const int rg = (int)((m + ROWS - 1) / ROWS);
     const int cg = (int)((n + kUpdCols - 1) / kUpdCols);
     const int64_t blocks = batch * rg * cg;
-    hipLaunchKernelGGL((lr_ef_update_kernel<RP, ROWS>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, st, m, n, r, U, V, RU, sign, Y, xhat, rg, cg);
+    if (x)
+        hipLaunchKernelGGL((lr_ef_update_kernel<RP, ROWS, true>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, st, m, n, r, U, V, RU, -1.0f, Y, nullptr, rg, cg, x,
+                           prev, A);
+    else
+        hipLaunchKernelGGL((lr_ef_update_kernel<RP, ROWS, false>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, st, m, n, r, U, V, RU, sign, Y, xhat, rg, cg,
+                           nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -298,10 +336,24 @@ hipError_t launch_lowrank_ef_update(int64_t batch, int64_t m, int64_t n, int r, 
     if (batch == 0)
         return hipSuccess;
     if (r <= 8)
-        return update_rp<8>(batch, m, n, r, U, V, RU, sign, Y, xhat, st);
+        return update_rp<8>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
     if (r <= 16)
-        return update_rp<16>(batch, m, n, r, U, V, RU, sign, Y, xhat, st);
-    return update_rp<32>(batch, m, n, r, U, V, RU, sign, Y, xhat, st);
+        return update_rp<16>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
+    return update_rp<32>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
+}
+
+hipError_t launch_lowrank_ef_residual_update(int64_t batch, int64_t m, int64_t n, int r,
+                                             const float *U, const float *V, const float *RU,
+                                             const uint16_t *x, uint16_t *prev, float *err,
+                                             uint16_t *A, hipStream_t st)
+{
+    if (batch == 0)
+        return hipSuccess;
+    if (r <= 8)
+        return update_rp<8>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
+    if (r <= 16)
+        return update_rp<16>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
+    return update_rp<32>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
 }
 
 }  // namespace cfz

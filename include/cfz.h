@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CFZ_ABI_VERSION 3
+#define CFZ_ABI_VERSION 4
 
 typedef enum {
     CFZ_OK = 0,
@@ -264,6 +264,31 @@ cfz_status cfz_lowrank_ef_compress(int64_t batch, int64_t m, int64_t n, int32_t 
                                    const uint16_t *x_bf16, uint16_t *prev_bf16, float *err,
                                    const float *Q0, float *U, float *V, float *RU,
                                    void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* The sender step with its last pass deferred: the call stops after the
+ * subspace iteration and leaves the residual r in err; the update
+ * err' = r - (U R_U) V^T is applied by the next deferred call, inside its own
+ * residual pass (pending = 1), which reads each element of err once instead of
+ * twice, or by cfz_lowrank_ef_flush.  pending = 0: err holds the carried error
+ * (as after cfz_lowrank_ef_warmup or cfz_lowrank_ef_compress); pending = 1: the
+ * previous call was deferred and U, V, RU still hold its factors, with the same
+ * batch, m, n and r.  For the same inputs a run of deferred calls followed by
+ * cfz_lowrank_ef_flush leaves prev, err, U, V and RU bit for bit as the same run
+ * of cfz_lowrank_ef_compress calls; the factors of each call are those of the
+ * plain call, so the receiver is unchanged.  Other arguments, workspace and
+ * errors as cfz_lowrank_ef_compress (Q0 may be the V buffer, the pending
+ * update only reads it), plus CFZ_ERR_SHAPE for pending not 0 or 1. */
+cfz_status cfz_lowrank_ef_compress_deferred(int64_t batch, int64_t m, int64_t n, int32_t r,
+                                            int32_t T, int32_t pending, const uint16_t *x_bf16,
+                                            uint16_t *prev_bf16, float *err, const float *Q0,
+                                            float *U, float *V, float *RU, void *workspace,
+                                            size_t ws_bytes, void *hip_stream);
+
+/* Applies a deferred call's pending update: err -= (U R_U) V^T, with the
+ * factors that call wrote (the same kernel and rounding as the plain sender).
+ * Errors: CFZ_ERR_NULL, CFZ_ERR_SHAPE, CFZ_ERR_ALIGN, CFZ_ERR_HIP. */
+cfz_status cfz_lowrank_ef_flush(int64_t batch, int64_t m, int64_t n, int32_t r, const float *U,
+                                const float *V, const float *RU, float *err, void *hip_stream);
 
 /* One receiver step (above): base += (U R_U) V^T; xhat_bf16 (nullable)
  * receives bf16(base') rounded to nearest even.

@@ -74,6 +74,9 @@ static int run(void)
     EXPECT(cfz_lowrank(2, 128, 192, 0, 2, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) ==
            CFZ_ERR_SHAPE);
     EXPECT(cfz_lowrank_ef_warmup(12, NULL, NULL, NULL, NULL, NULL) == CFZ_ERR_SHAPE);
+    EXPECT(cfz_lowrank_ef_compress_deferred(2, 128, 192, 8, 2, 2, NULL, NULL, NULL, NULL, NULL,
+                                            NULL, NULL, NULL, 0, NULL) == CFZ_ERR_SHAPE);
+    EXPECT(cfz_lowrank_ef_flush(2, 128, 192, 8, NULL, NULL, NULL, NULL, NULL) == CFZ_ERR_NULL);
     EXPECT(cfz_stream_copy(NULL, NULL, 0, NULL) == CFZ_OK);
     return 0;
 }

@@ -14,10 +14,10 @@ MISALIGNED = 0x10008
 
 def test_library_exports_every_declared_function():
     names = cfz.header_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for name in names:
         assert hasattr(cfz._lib, name), f"libcfz.so does not export {name}"
-    assert cfz.cfz_abi_version() == 3
+    assert cfz.cfz_abi_version() == 4
 
 
 def test_status_strings():
@@ -158,6 +158,29 @@ def test_lowrank_ef_validation():
     assert comp(ws_bytes=need - 1) == cfz.CFZ_ERR_WORKSPACE
     assert comp(ws=ALIGNED + 16) == cfz.CFZ_ERR_ALIGN
     assert comp(batch=0, x=None) == cfz.CFZ_OK
+
+    def comp_d(pending=1, batch=b, mm=m, nn=n, rr=r, T=1, x=ALIGNED, prev=ALIGNED, err=ALIGNED,
+               Q0=ALIGNED, U=ALIGNED, V=ALIGNED, RU=ALIGNED, ws=ALIGNED, ws_bytes=need):
+        return lib.cfz_lowrank_ef_compress_deferred(batch, mm, nn, rr, T, pending, x, prev, err,
+                                                    Q0, U, V, RU, ws, ws_bytes, None)
+
+    assert comp_d(pending=2) == cfz.CFZ_ERR_SHAPE
+    assert comp_d(pending=-1) == cfz.CFZ_ERR_SHAPE
+    assert comp_d(nn=196) == cfz.CFZ_ERR_SHAPE
+    assert comp_d(T=-1) == cfz.CFZ_ERR_SHAPE
+    assert comp_d(U=None) == cfz.CFZ_ERR_NULL
+    assert comp_d(pending=0, err=MISALIGNED) == cfz.CFZ_ERR_ALIGN
+    assert comp_d(ws_bytes=need - 1) == cfz.CFZ_ERR_WORKSPACE
+    assert comp_d(batch=0, x=None) == cfz.CFZ_OK
+
+    def flush(batch=b, U=ALIGNED, V=ALIGNED, RU=ALIGNED, err=ALIGNED, rr=r, nn=n):
+        return lib.cfz_lowrank_ef_flush(batch, m, nn, rr, U, V, RU, err, None)
+
+    assert flush(err=None) == cfz.CFZ_ERR_NULL
+    assert flush(V=MISALIGNED) == cfz.CFZ_ERR_ALIGN
+    assert flush(rr=0) == cfz.CFZ_ERR_SHAPE
+    assert flush(nn=196) == cfz.CFZ_ERR_SHAPE
+    assert flush(batch=0, err=None) == cfz.CFZ_OK
 
     def dec(batch=b, U=ALIGNED, V=ALIGNED, RU=ALIGNED, base=ALIGNED, xhat=None, rr=r):
         return lib.cfz_lowrank_ef_decompress(batch, m, n, rr, U, V, RU, base, xhat, None)
@@ -316,6 +339,11 @@ def test_binding_rejects_undersized_tensors_before_any_launch():
     with pytest.raises(ValueError, match="err"):
         cfz.cfz_lowrank_ef_compress(b, m, nn, r, 1, A, A, torch.empty(b * m * nn - 1), Q0, U, V,
                                     RU, ws)
+    with pytest.raises(ValueError, match="err"):
+        cfz.cfz_lowrank_ef_compress_deferred(b, m, nn, r, 1, 1, A, A, torch.empty(b * m * nn - 1),
+                                             Q0, U, V, RU, ws)
+    with pytest.raises(ValueError, match="err"):
+        cfz.cfz_lowrank_ef_flush(b, m, nn, r, U, V, RU, torch.empty(b * m * nn - 1))
     with pytest.raises(ValueError, match="base"):
         cfz.cfz_lowrank_ef_decompress(b, m, nn, r, U, V, RU, torch.empty(b * m * nn - 1))
     with pytest.raises(ValueError, match="prev"):

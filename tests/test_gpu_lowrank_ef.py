@@ -254,3 +254,40 @@ def test_graph_replay_matches_eager_every_replay():
                                b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_), \
                 f"replay {t}: {name} differs from the eager step"
     say(f"  {steps} replays bit-identical to eager steps")
+
+
+@pytest.mark.parametrize("batch,m,n,r,T,warm", [(2, 130, 264, 16, 2, False),
+                                                (1, 1100, 264, 32, 1, True),
+                                                (3, 96, 136, 5, 2, True),
+                                                (57, 1024, 3072, 16, 2, True)])
+def test_deferred_sender_matches_plain_bit_for_bit(batch, m, n, r, T, warm):
+    """The deferred sender (each step's update applied inside the next step's residual pass)
+    against the plain sender on the same inputs: the factors, prev and the bf16 residual after
+    every step, and err after each flush, equal bit for bit.  One flush in the middle of the
+    run, so that steps after it start with nothing pending."""
+    steps = 6
+    say(f"[gpu] lowrank-ef deferred batch={batch} m={m} n={n} r={r} T={T} warm={warm}")
+    st = LowrankDrift(batch, m, n, seed=31 + r, device=DEV)
+    x = st.next()
+    plain = cfz.LowrankSender(batch, m, n, r, x0=x)
+    dfr = cfz.LowrankSender(batch, m, n, r, x0=x, deferred=True)
+    for t in range(1, steps):
+        x = st.next()
+        q0 = gaussian_q0(batch, n, r, seed=60 + t, device=DEV)
+        plain.compress(x, plain.V if warm and t > 1 else q0, T)
+        dfr.compress(x, dfr.V if warm and t > 1 else q0, T)
+        if t == 3:
+            dfr.flush()
+            assert not dfr.pending
+        torch.cuda.synchronize()
+        for name, a_, b_ in (("U", dfr.U, plain.U), ("V", dfr.V, plain.V),
+                             ("RU", dfr.RU, plain.RU),
+                             ("prev", dfr.prev.view(torch.int16), plain.prev.view(torch.int16)),
+                             ("A", dfr.residual_bf16().view(torch.int16),
+                              plain.residual_bf16().view(torch.int16))):
+            assert torch.equal(a_, b_), f"step {t}: {name} differs from the plain sender"
+        if t == 3:
+            assert torch.equal(dfr.err, plain.err), f"step {t}: err after the flush"
+    dfr.flush()
+    torch.cuda.synchronize()
+    assert torch.equal(dfr.err, plain.err), "err after the final flush"
