@@ -17,9 +17,11 @@
 //                           bf16(Y') too (8 or 10 bytes per element, HBM bound).  The
 //                           rank-r product is a contraction over r <= 32, evaluated as
 //                           U (V R_U^T)^T on v_mfma_f32_16x16x4_f32: a work-group owns
-//                           256 columns of 256 rows (1024 at r = 32), forms its columns'
-//                           rows of V R_U^T once in registers and streams the block's
-//                           rows of Y and U.
+//                           256 columns of 64 rows (128 at r > 16), forms its columns'
+//                           rows of V R_U^T once on MFMA, in registers, and streams the
+//                           block's rows of Y and U.  Its RESID form is the sender's
+//                           update deferred into the next step's residual pass
+//                           (24 -> 16 bytes per element over the two passes).
 //                           Sender and receiver run the same kernel on the same factors,
 //                           so their reconstructions agree bit for bit.
 
@@ -35,7 +37,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kUpdRows = 256;  // rows of Y per work-group of the update at r <= 16
+constexpr int kUpdRows = 64;   // rows of Y per work-group of the update at r <= 16
 constexpr int kUpdCols = 256;  // columns per work-group (each wave: 64 = 4 tiles of 16)
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -116,13 +118,22 @@ __device__ __forceinline__ void load_floats(const float *p, int valid, bool vec,
 }
 
 // Y = Y +- U (V R_U^T)^T for one ROWS x 256 block of one matrix; the same product as
-// (U R_U) V^T.  The contraction index k is split so that lane group g = l / 16 holds
-// k = g J + j in step j (J = RP / 4): its operands are J consecutive floats of a row of
-// U or of V R_U^T.  Wave w owns columns 64 w .. 64 w + 63 of the block (4 tiles of 16);
-// it forms its tiles' rows of V R_U^T once, in registers, then walks down the rows 32 at
-// a time.  The MFMA result holds 16 rows x 4 columns per lane group, so each lane would
-// touch 64-byte pieces of 16 rows; instead the wave passes its 32 x 64 result through
-// its own LDS region and reads and writes Y as 4 rows x 256 bytes per instruction.
+// (U R_U) V^T.  Wave w owns columns 64 w .. 64 w + 63 of the block (4 tiles of 16).
+//   prologue: the wave forms V R_U^T for its tiles on MFMA as R_U V^T (16 k x 16 columns
+//             per tile, K = r over l), lane group g holding l = g S + s in step s
+//             (S = RP / 4).  The result leaves lane (c, g) with W[column c][k = 16 kt + 4 g
+//             + v] in item v of k-tile kt -- exactly the A operand of the main product when
+//             its step j gives lane group g the index k = 16 (j / 4) + 4 g + j % 4, so no
+//             layout change is needed, and U's operands are 4 consecutive floats of a row.
+//   main loop: 32 rows per step; the MFMA result holds 16 rows x 4 columns per lane
+//             group, so each lane would touch 64-byte pieces of 16 rows; instead the wave
+//             passes its 32 x 64 result through its own LDS region and reads and writes Y as
+//             4 rows x 256 bytes per instruction.  The next step's loads are issued before
+//             this step's stores (vector memory counters retire in order, so waiting for a
+//             step's loads never waits for the stores queued behind them), and the first
+//             step's loads before the prologue.
+// Short blocks (64 rows at r <= 16, 128 at r = 32) keep many work-groups in the grid; the
+// MFMA prologue is what makes them affordable (see the launcher).
 // RESID: the sender's pending update fused into the next step's residual pass -- Y is
 // the carried error's buffer holding the previous residual r0; each element becomes
 // e = r0 - D (the value the update alone would store), then the new residual
@@ -136,9 +147,10 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                     int col_groups, const uint16_t *__restrict__ x, uint16_t *__restrict__ prev,
                     uint16_t *__restrict__ A)
 {
-    constexpr int J = RP / 4;
+    static_assert(RP == 16 || RP == 32, "rank padded to 16 or 32");
+    static_assert(ROWS % 32 == 0, "whole 32-row steps");
+    constexpr int J = RP / 4, KT = RP / 16, S = RP / 4;
     constexpr int SD = 64 + 4;  // padded row of a wave's result tile (floats)
-    __shared__ float sR[RP][RP + 1];
     __shared__ f32x4 sD[4][32][SD / 4];
 
     const int groups = row_groups * col_groups;
@@ -150,51 +162,18 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
     const float *Ub = U + b * m * r;
     const float *Vb = V + b * n * r;
     const float *Rb = RU + b * r * r;
-
-    for (int i = threadIdx.x; i < RP * RP; i += kThreads) {
-        const int k = i / RP, l = i % RP;
-        sR[k][l] = (k < r && l < r) ? Rb[k * r + l] : 0.0f;
-    }
-    __syncthreads();
-
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, g = lane >> 4, li = lane & 15;
-    // this lane's operands of V R_U^T: row c = col0 + 64 w + 16 ct + li, k = g J + j,
-    // accumulated over l = 0 .. r-1 in order; row c of V read whole with vector loads
-    float vop[4][J];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int64_t c = col0 + 64 * wave + 16 * ct + li;
-        float vr[RP];
-        if (c < n)
-            load_floats<RP>(Vb + c * r, r, r == RP, vr);
-        else
-#pragma unroll
-            for (int l = 0; l < RP; ++l)
-                vr[l] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int l = 0; l < RP; ++l)
-                if (l < r)
-                    acc = __builtin_fmaf(vr[l], sR[g * J + j][l], acc);
-            vop[ct][j] = acc;
-        }
-    }
-
     float *Yb = Y + b * m * n;
     uint16_t *Xb = xhat ? xhat + b * m * n : nullptr;
-    // streaming layout: instruction k of row block h covers rows 16 h + 4 k + lane / 16,
+    // streaming layout: instruction k of row tile h covers rows 16 h + 4 k + lane / 16,
     // this lane's 4 columns being 4 (lane % 16) of the wave's 64
     const int64_t col = col0 + 64 * wave + 4 * li;
     const bool col_ok = col < n;  // n % 8 == 0: all four or none
-    const int kvalid = r - g * J;
+    const bool vec = r == RP;     // rows of U, V and R_U 16-byte aligned, no tail
 
-    for (int rb = 0; rb < ROWS / 16; rb += 2) {
-        if (row0 + 16 * rb >= m)
-            break;  // uniform over the work-group
-        f32x4 yv[2][4];
-        u32x2 xv[2][4], pv[2][4];
+    f32x4 yv[2][4];
+    u32x2 xv[2][4], pv[2][4];
+    auto load_step = [&](int rb) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -209,16 +188,65 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                     pv[h][k] = ok ? __builtin_nontemporal_load((const u32x2 *)(prev + o)) : u32x2{0, 0};
                 }
             }
+    };
+    load_step(0);
+
+    float vop[4][J];
+    {
+        float ra[KT][S];
+        const int lv = r - g * S;  // valid l of this lane group
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int kr = 16 * kt + li;
+            if (kr < r && lv > 0)
+                load_floats<S>(Rb + kr * r + g * S, lv, vec, ra[kt]);
+            else
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    ra[kt][s] = 0.0f;
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int64_t c = col0 + 64 * wave + 16 * ct + li;
+            float vb[S];
+            if (c < n && lv > 0)
+                load_floats<S>(Vb + c * r + g * S, lv, vec, vb);
+            else
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    vb[s] = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                f32x4 w = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    w = mfma4(ra[kt][s], vb[s], w);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    vop[ct][4 * kt + v] = w[v];
+            }
+        }
+    }
+
+    for (int rb = 0; rb < ROWS / 16; rb += 2) {
+        if (row0 + 16 * rb >= m)
+            break;  // uniform over the work-group
         float uop[2][J];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t row = row0 + 16 * (rb + h) + li;
-            if (row < m)
-                load_floats<J>(Ub + row * r + g * J, kvalid, r == RP, uop[h]);
-            else
 #pragma unroll
-                for (int j = 0; j < J; ++j)
-                    uop[h][j] = 0.0f;
+            for (int kt = 0; kt < KT; ++kt) {
+                const int kv = r - (16 * kt + 4 * g);
+                float u4[4];
+                if (row < m && kv > 0)
+                    load_floats<4>(Ub + row * r + 16 * kt + 4 * g, kv, vec, u4);
+                else
+                    u4[0] = u4[1] = u4[2] = u4[3] = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    uop[h][4 * kt + v] = u4[v];
+            }
         }
         // D tiles (row li, columns 16 ct + 4 g) into the wave's LDS tile
 #pragma unroll
@@ -235,6 +263,20 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 yc[2][4];
+        u32x2 xc[2][4], pc[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                yc[h][k] = yv[h][k];
+                if constexpr (RESID) {
+                    xc[h][k] = xv[h][k];
+                    pc[h][k] = pv[h][k];
+                }
+            }
+        if (rb + 2 < ROWS / 16 && row0 + 16 * (rb + 2) < m)
+            load_step(rb + 2);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -250,8 +292,8 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                     f32x4 ev;
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        ev[v] = yv[h][k][v] - d[v];
-                    const u32x2 xq = xv[h][k], pq = pv[h][k];
+                        ev[v] = yc[h][k][v] - d[v];
+                    const u32x2 xq = xc[h][k], pq = pc[h][k];
                     o[0] = (bf16_lo(xq[0]) - bf16_lo(pq[0])) + ev[0];
                     o[1] = (bf16_hi(xq[0]) - bf16_hi(pq[0])) + ev[1];
                     o[2] = (bf16_lo(xq[1]) - bf16_lo(pq[1])) + ev[2];
@@ -264,7 +306,7 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                 } else {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        o[v] = sign > 0.0f ? yv[h][k][v] + d[v] : yv[h][k][v] - d[v];
+                        o[v] = sign > 0.0f ? yc[h][k][v] + d[v] : yc[h][k][v] - d[v];
                     __builtin_nontemporal_store(o, (f32x4 *)(Yb + row * n + col));
                     if (Xb)
                         __builtin_nontemporal_store(
@@ -272,23 +314,20 @@ lr_ef_update_kernel(int64_t m, int64_t n, int r, const float *__restrict__ U,
                             (u32x2 *)(Xb + row * n + col));
                 }
             }
-        // the next block's writes to the tile come after these reads
+        // the next step's writes to the tile come after these reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
-// Rows per work-group: each work-group first forms its columns' rows of V R_U^T
-// (r x r work per column), so at r = 32 taller blocks amortise that better
-// (1024 rows: 334 / 408 us per sender / receiver call at 57 x 1024 x 3072,
-// against 423 / 493 us with 256); at r <= 16, 256 rows is fastest.  Reading each
-// row of V whole with vector loads (rather than one float of 16 rows per load)
-// took the r = 16 update from 290 to 277 us (367 to 357 with the bf16 output);
-// loading the next 32-row block ahead, or a resident grid walking equal shares of
-// 32 x 256 units, were no faster (the first costs a wave of occupancy).
+// Rows per work-group.  At 57 x 1024 x 3072, per sender / receiver / fused call: r = 16
+// with 64 rows 249 / 321 / 530 us against 264 / 342 / 568 with 256; r = 32 with 128 rows
+// 285 / 353 / 563 us.  Short blocks pay when the prologue is cheap: with V R_U^T formed by
+// per-lane fma chains from an LDS copy of R_U, 64-row blocks took 316 us against 271 with
+// 256 (sender, r = 16), and the old 256-row kernel 276 / 355 / 578 us.
 template <int RP>
-constexpr int upd_rows() { return RP == 32 ? 4 * kUpdRows : kUpdRows; }
+constexpr int upd_rows() { return RP == 32 ? 2 * kUpdRows : kUpdRows; }
 
 template <int RP>
 hipError_t update_rp(int64_t batch, int64_t m, int64_t n, int r, const float *U, const float *V,
@@ -335,8 +374,6 @@ hipError_t launch_lowrank_ef_update(int64_t batch, int64_t m, int64_t n, int r, 
 {
     if (batch == 0)
         return hipSuccess;
-    if (r <= 8)
-        return update_rp<8>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
     if (r <= 16)
         return update_rp<16>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
     return update_rp<32>(batch, m, n, r, U, V, RU, sign, Y, xhat, nullptr, nullptr, nullptr, st);
@@ -349,8 +386,6 @@ hipError_t launch_lowrank_ef_residual_update(int64_t batch, int64_t m, int64_t n
 {
     if (batch == 0)
         return hipSuccess;
-    if (r <= 8)
-        return update_rp<8>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
     if (r <= 16)
         return update_rp<16>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
     return update_rp<32>(batch, m, n, r, U, V, RU, -1.0f, err, nullptr, x, prev, A, st);
