@@ -21,8 +21,8 @@ Further legs in the same JSON line: other launch granularities (per tensor,
 16 tensors), the three error-feedback readings with their receiver error,
 bf16 state, int2 group-32 over all tensors in one launch, the CogVideoX-2b
 share, the subspace iteration at r = 8/16/32, the rank-r compressor inside
-error feedback (random or warm-started Q0), and the CPU oracle on a bounded
-sample of the same workload.
+error feedback (plain and deferred sender; random or warm-started Q0), and the
+CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 27] [--warmup 1] [--streams 3] [--no-cpu-baseline]
 """
@@ -222,7 +222,9 @@ def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
 def bench_lowrank_ef(cfz, torch, dev, batch=57, m=1024, n=3072, r=16, T=2, steps=6):
     """The rank-r compressor inside error feedback on 57 layers of 1024 x 3072 per step:
     activations drift by rank 16 + noise per step.  One step = one sender call (residual,
-    subspace iteration, error update) and one receiver call (base update + bf16 output).
+    subspace iteration, error update) and one receiver call (base update + bf16 output);
+    timed again with the deferred sender (each step's error update applied inside the next
+    step's residual pass; the last one flushed after the timed steps).
     Timed with a fresh random Q0 per step; then, over the same consecutive steps, the
     receiver's relative error ||base - x|| / ||x|| with random or warm-started Q0 (the
     previous step's V) at T = 1 and T = 2."""
