@@ -157,6 +157,23 @@ __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2 /*nt*/));
 }
 
+// Rows 8 kb .. 8 kb + 7 of column c of an fp32 [L][r] matrix as one operand slot, split
+// into bf16 hi (lo = false) or the bf16 rounding of what hi misses (lo = true); rows past
+// L and columns past r are zeros.  The same values the operand-layout kernel stores.
+__device__ __forceinline__ bf16x8 slot_from_f32(const float *M, int64_t L, int r, int64_t kb,
+                                                int c, bool lo)
+{
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = 8 * kb + i;
+        const float q = (row < L && c < r) ? M[row * r + c] : 0.0f;
+        const __bf16 h = (__bf16)q;
+        o[i] = lo ? (__bf16)(q - (float)h) : h;
+    }
+    return o;
+}
+
 // ------------------------------------------------------------------ Y = A Q
 
 constexpr int kPipe = 4;                        // register stages of the A-streaming pipelines
@@ -512,7 +529,7 @@ template <int RP>
 __global__ void __launch_bounds__(kAtaThreads)
 lr_ata_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
               size_t layer_bytes, size_t off_qops, size_t off_z, int64_t np, int splits,
-              int64_t split_rows)
+              int64_t split_rows, const float *__restrict__ /* q0: the r <= 8 kernel's only */)
 {
     static_assert(RP == 16, "the one-pass product keeps Z in registers only for RP = 16");
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -663,7 +680,9 @@ lr_ata_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8
 // row per wave to load, 6 x 16 bytes per lane in flight); phase 2 likewise
 // carries Y hi and Y lo as columns 0..7 and 8..15 of one K = 16 MFMA.  The two
 // halves of each product are added across lanes li and li + 8 (Y before the
-// cross-wave sum, Z once at the end).
+// cross-wave sum, Z once at the end).  q0 non-null (the first iteration): the
+// lanes split the fp32 sample into its hi and lo operands themselves, the values
+// the operand-layout kernel would have stored, and that launch is skipped.
 constexpr int kAta8Panel = 16;
 static_assert(kAtaWaves == kAta8Panel && kAtaMaxN == 8 * 64 * 6,
               "each wave loads one full-width panel row in 6 16-byte loads per lane");
@@ -672,7 +691,7 @@ template <int RP>
 __global__ void __launch_bounds__(kAtaThreads)
 lr_ata8_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint8_t *__restrict__ ws,
                size_t layer_bytes, size_t off_qops, size_t off_z, int64_t np, int splits,
-               int64_t split_rows)
+               int64_t split_rows, const float *__restrict__ q0)
 {
     static_assert(RP == 16, "columns 0..7 and 8..15 of the padded width carry hi and lo");
     constexpr int kChunks = 6;
@@ -728,8 +747,12 @@ lr_ata8_kernel(const uint16_t *__restrict__ A, int64_t m, int64_t n, int r, uint
     bf16x8 qp[kAtaMaxBlocks];
 #pragma unroll
     for (int j = 0; j < kAtaMaxBlocks; ++j) {
-        const int64_t slot = (int64_t)(4 * (kb0 + (j < kbn ? j : 0)) + g) * RP + (li & 7);
-        qp[j] = j < kbn ? (li < 8 ? qhi[slot] : qlo[slot]) : bf16x8{};
+        const int64_t kb = 4 * (kb0 + (j < kbn ? j : 0)) + g, slot = kb * RP + (li & 7);
+        if (q0)  // the first iteration reads the fp32 sample itself
+            qp[j] = j < kbn ? slot_from_f32(q0 + (int64_t)b * n * r, n, r, kb, li & 7, li >= 8)
+                            : bf16x8{};
+        else
+            qp[j] = j < kbn ? (li < 8 ? qhi[slot] : qlo[slot]) : bf16x8{};
     }
 
     const int tailc = (32 * nb - (int)n) / 8;
@@ -1862,7 +1885,9 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
         if ((e = run_orth<RP>(Ly, a.batch, a.Q0, a.n * a.r, a.n, a.r, ws, a.V, a.n * a.r, true,
                               nullptr, st)) != hipSuccess)
             return e;
-    } else {
+    } else if (!(RP == 16 && Ly.splits > 0 && a.r <= 8)) {
+        // (at r <= 8 the one-pass product reads Q0 itself: 8 us less per call; at r = 9..16
+        // the same conversion in that kernel's prologue cost it more than the launch saves)
         const int64_t slots = (Ly.np / 8) * RP, total = slots * a.batch;
         hipLaunchKernelGGL((lr_ops_kernel<RP>), dim3((unsigned)((total + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, st, a.Q0, a.n * a.r, a.n, Ly.np, a.r, ws,
@@ -1877,7 +1902,8 @@ hipError_t run_lowrank(const LowrankArgs &a, hipStream_t st)
                 hipLaunchKernelGGL((a.r <= 8 ? lr_ata8_kernel<RP> : lr_ata_kernel<RP>),
                                    dim3((unsigned)(Ly.splits * a.batch)), dim3(kAtaThreads), 0, st,
                                    a.A, a.m, a.n, a.r, ws, Ly.layer_bytes, Ly.off_qops,
-                                   Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows);
+                                   Ly.off_mf, Ly.np, Ly.splits, Ly.split_rows,
+                                   t == 0 && a.r <= 8 ? a.Q0 : nullptr);
         }
         if (Ly.splits == 0) {
             hipLaunchKernelGGL((lr_aq_kernel<RP, true>), dim3((unsigned)(aq_blocks * a.batch)),
