@@ -234,7 +234,7 @@ size_t cfz_lowrank_noalloc_max_bytes(void);
  * factors their reconstructions agree bit for bit.
  * Layouts: x, prev, xhat bf16 and err, base fp32, all [batch][m][n]; U, V, RU
  * as for cfz_lowrank.  Sizes as for cfz_lowrank, plus two launch-size limits:
- * batch * ceil(m / 256) * ceil(n / 256) < 2^31 and batch * m * n / 1024 < 2^31
+ * batch * ceil(m / 64) * ceil(n / 256) < 2^31 and batch * m * n / 1024 < 2^31
  * (integer division).  Every pointer 16-byte aligned; the caller owns all
  * memory.  Calls are asynchronous on hip_stream; tensors of one state must not
  * be used on two streams at once. */

@@ -158,6 +158,9 @@ def test_lowrank_ef_validation():
     assert comp(ws_bytes=need - 1) == cfz.CFZ_ERR_WORKSPACE
     assert comp(ws=ALIGNED + 16) == cfz.CFZ_ERR_ALIGN
     assert comp(batch=0, x=None) == cfz.CFZ_OK
+    # launch size: batch * ceil(m / 64) * ceil(n / 256) must stay below 2^31
+    assert comp(batch=1 << 20, mm=1 << 17, nn=8, rr=1) == cfz.CFZ_ERR_SHAPE
+    assert comp(batch=(1 << 20) - 1, mm=1 << 17, nn=8, rr=1) == cfz.CFZ_ERR_WORKSPACE
 
     def comp_d(pending=1, batch=b, mm=m, nn=n, rr=r, T=1, x=ALIGNED, prev=ALIGNED, err=ALIGNED,
                Q0=ALIGNED, U=ALIGNED, V=ALIGNED, RU=ALIGNED, ws=ALIGNED, ws_bytes=need):
