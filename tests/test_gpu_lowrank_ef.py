@@ -291,3 +291,45 @@ def test_deferred_sender_matches_plain_bit_for_bit(batch, m, n, r, T, warm):
     dfr.flush()
     torch.cuda.synchronize()
     assert torch.equal(dfr.err, plain.err), "err after the final flush"
+
+
+def test_deferred_sender_graph_replay_matches_eager():
+    """The deferred sender's steady-state call (the pending update fused into the residual
+    pass, then the subspace iteration) captured once in a HIP graph and replayed step after
+    step gives the bits of the same deferred steps run eagerly, and after a final flush the
+    carried error of the plain sender."""
+    b, m, n, r, T, steps = 2, 192, 256, 16, 2, 5
+    say("[gpu] lowrank-ef deferred graph replay")
+    st = LowrankDrift(b, m, n, seed=23, device=DEV)
+    xs = [st.next() for _ in range(steps + 2)]
+    q0s = [gaussian_q0(b, n, r, seed=70 + t, device=DEV) for t in range(steps + 2)]
+    es = cfz.LowrankSender(b, m, n, r, x0=xs[0], deferred=True)
+    gs = cfz.LowrankSender(b, m, n, r, x0=xs[0], deferred=True)
+    ps = cfz.LowrankSender(b, m, n, r, x0=xs[0])
+    # the first step leaves an update pending on every deferred sender
+    for s_ in (es, gs, ps):
+        s_.compress(xs[1], q0s[1], T)
+    xin, qin = torch.empty_like(xs[0]), torch.empty_like(q0s[0])
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        cfz.cfz_lowrank_ef_compress_deferred(b, m, n, r, T, 1, xin, gs.prev, gs.err, qin, gs.U,
+                                             gs.V, gs.RU, gs.ws)
+    torch.cuda.synchronize()
+    for t in range(2, steps + 2):
+        es.compress(xs[t], q0s[t], T)
+        ps.compress(xs[t], q0s[t], T)
+        xin.copy_(xs[t])
+        qin.copy_(q0s[t])
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a_, b_ in (("U", gs.U, es.U), ("V", gs.V, es.V), ("RU", gs.RU, es.RU),
+                             ("err", gs.err, es.err),
+                             ("prev", gs.prev.view(torch.int16), es.prev.view(torch.int16))):
+            assert torch.equal(a_, b_), f"replay {t}: {name} differs from the eager deferred step"
+    cfz.cfz_lowrank_ef_flush(b, m, n, r, gs.U, gs.V, gs.RU, gs.err)
+    torch.cuda.synchronize()
+    assert torch.equal(gs.err, ps.err), "flushed err differs from the plain sender's"
+    say(f"  {steps} deferred replays bit-identical to eager steps")
