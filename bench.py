@@ -131,7 +131,7 @@ def cpu_baseline(xs_host, bits, group, budget_s=20.0):
     return out
 
 
-def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps):
+def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps, label=None):
     """All tensors of a step in one compress and one decode launch (rows = tensors x tokens)."""
     n = rows * cols
     dev = X.device
@@ -158,8 +158,9 @@ def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps):
     cfz.cfz_state_destroy(snd)
     cfz.cfz_state_destroy(rcv)
     bc, bd = algorithmic_bytes(bits, group)
-    return {"workload": f"flux-share all 114 tensors in one launch ({rows}x{cols}), "
-                        f"int{bits} g{group}, delta", "steps": steps,
+    if label is None:
+        label = f"flux-share all 114 tensors in one launch ({rows}x{cols})"
+    return {"workload": f"{label}, int{bits} g{group}, delta", "steps": steps,
             "activation_GB/s": round(2 * n / (tc + td) / 1e9, 2),
             "compress": {"us": round(tc * 1e6, 2), "GB/s": round(bc * n / tc / 1e9, 1),
                          "frac_hbm_peak": round(bc * n / tc / 1e9 / HBM_PEAK_GBS, 4)},
@@ -429,7 +430,8 @@ def bench_error_trajectory(cfz, torch, X, slots, rows, cols, bits=4, group=64):
 def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
     """CogVideoX-2b share at sequence-parallel degree 4: 30 layers x {K, V} of 4388 x 1920
     bf16 (AR(1), alpha 0.97), DELTA, one grouped compress and one grouped decode launch per
-    layer (its K and V), replayed from HIP graphs."""
+    layer (its K and V), replayed from HIP graphs; then the same tensors as one contiguous
+    batch, one compress and one decode launch per step."""
     from synth import SPECS, AR1Stream
 
     sp = SPECS["cogvideox"]
@@ -500,6 +502,11 @@ def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
         cfz.cfz_state_destroy(h)
     bc, bd = algorithmic_bytes(bits, group)
     per = 2 * n  # elements per launch
+    del prev, err, base, codes, scales
+    # the same tensors as one contiguous batch: one compress and one decode launch per step
+    batched = bench_batched(cfz, torch, X.view(pool + 1, T * n), pool + 1, T * rows, cols, bits,
+                            group, steps, label=f"cogvideox-2b-share all {T} tensors in one "
+                                                f"launch ({T * rows}x{cols})")
     return {"workload": f"cogvideox-2b-share {T} tensors of {rows}x{cols}, int{bits} g{group}, "
                         "delta, one grouped launch per layer (K and V), replayed from HIP graphs",
             "steps": steps,
@@ -507,7 +514,8 @@ def bench_cogvideox(cfz, torch, dev, bits, group, steps=10, pool=4):
             "compress": {"avg_launch_us": round(tc * 1e6, 3), "GB/s": round(bc * per / tc / 1e9, 1),
                          "frac_hbm_peak": round(bc * per / tc / 1e9 / HBM_PEAK_GBS, 4)},
             "decode": {"avg_launch_us": round(td * 1e6, 3), "GB/s": round(bd * per / td / 1e9, 1),
-                       "frac_hbm_peak": round(bd * per / td / 1e9 / HBM_PEAK_GBS, 4)}}
+                       "frac_hbm_peak": round(bd * per / td / 1e9 / HBM_PEAK_GBS, 4)},
+            "one_launch_per_step": batched}
 
 
 def lowrank_cpu_baseline(A_layer, batch, T=2, ranks=(8, 16, 32)):
