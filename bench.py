@@ -17,7 +17,8 @@ with HIP events on the stream the kernels run on, in a second timed pass of
 the same launches on one stream (events around the compress and the decode
 phase of each step; overlapped launches have no duration of their own).
 
-Further legs in the same JSON line: other launch granularities (per tensor,
+Further legs in the same JSON line: the tiny configuration's per-call latency, other
+launch granularities (per tensor,
 16 tensors), the three error-feedback readings with their receiver error,
 bf16 state, int2 group-32 over all tensors in one launch, the CogVideoX-2b
 share, the subspace iteration at r = 8/16/32, the rank-r compressor inside
@@ -166,6 +167,53 @@ def bench_batched(cfz, torch, X, slots, rows, cols, bits, group, steps, label=No
                          "frac_hbm_peak": round(bc * n / tc / 1e9 / HBM_PEAK_GBS, 4)},
             "decode": {"us": round(td * 1e6, 2), "GB/s": round(bd * n / td / 1e9, 1),
                        "frac_hbm_peak": round(bd * n / td / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def bench_tiny(cfz, torch, dev, reps=200):
+    """The tiny configuration (one 256 x 512 tensor, int4 g64, DELTA, its 4 seeded steps): a
+    latency figure, not a bandwidth one -- the tensor sits in cache.  Each compress and decode
+    call launched back to back reps times, eagerly and from a HIP graph of reps launches."""
+    from synth import SPECS, AR1Stream
+
+    sp = SPECS["tiny"]
+    st = AR1Stream.from_spec(sp, seed=0, device=dev)
+    xs = [st.next()[0].contiguous() for _ in range(sp.steps)]
+    snd = cfz.Sender(sp.rows, sp.cols, 4, 64, x0=xs[0])
+    rcv = cfz.Receiver(sp.rows, sp.cols, 4, 64, x0=xs[0])
+    out = {"workload": f"tiny {sp.rows}x{sp.cols} int4 g64 delta, {sp.steps} steps"}
+
+    def calls(k):
+        x = xs[1 + k % (sp.steps - 1)]
+        cfz.cfz_compress(snd.handle, x, snd.codes, snd.scales)
+        cfz.cfz_decompress(rcv.handle, snd.codes, snd.scales)
+
+    for k in range(reps // 10):
+        calls(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(reps):
+        calls(k)
+    e1.record()
+    torch.cuda.synchronize()
+    out["eager_us_per_compress_plus_decode"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(reps):
+            calls(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    out["graph_us_per_compress_plus_decode"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    snd.close()
+    rcv.close()
+    return out
 
 
 def bench_lowrank(cfz, torch, dev, batch=57, m=1024, n=3072, T=2, reps=5):
@@ -941,6 +989,8 @@ def main():
         print("[bench] batched int2 leg", file=sys.stderr, flush=True)
         line["batched_int2_g32"] = bench_batched(cfz, torch, X, slots, T * rows, cols, 2, 32,
                                                  steps=min(K, 10))
+    print("[bench] tiny-configuration latency leg", file=sys.stderr, flush=True)
+    line["tiny_latency"] = bench_tiny(cfz, torch, dev)
     if not args.no_cogvideox:
         for cb, cg in ((4, 64), (2, 32)):
             print(f"[bench] CogVideoX-share leg, int{cb} g{cg}", file=sys.stderr, flush=True)
