@@ -833,6 +833,10 @@ def main():
                                          "decode": load_traffic("decode_bf16_state", wl16)},
             "activation_GB/s": round(2 * n * T * kb / r_ov["elapsed"] / 1e9, 2),
             "activation_GB/s_one_stream": round(2 * n * T * kb / r_["elapsed"] / 1e9, 2),
+            "step_hbm": {"GB/s": round((bc16 + bd16) * n * T * kb / r_ov["elapsed"] / 1e9, 1),
+                         "frac_hbm_peak": round((bc16 + bd16) * n * T * kb / r_ov["elapsed"] / 1e9
+                                                / HBM_PEAK_GBS, 4),
+                         "bytes_per_elem": bc16 + bd16},
             "compress": {"avg_launch_us": round(r_["t_comp"] / nl * 1e6, 3),
                          "GB/s": round(c16, 1), "frac_hbm_peak": round(c16 / HBM_PEAK_GBS, 4),
                          "bytes_per_elem": bc16},
@@ -974,6 +978,10 @@ def main():
         "schedules": {  # activation GB/s of the same per-layer launches
             f"{nstreams}_streams": round(value, 2),
             "1_stream": round(2 * n * T * K / kres["elapsed"] / 1e9, 2)},
+        # the whole step's algorithmic bytes (compress + decode of every tensor) over its time
+        "step_hbm": {"GB/s": round((bc + bd) * n * T * K / elapsed / 1e9, 1),
+                     "frac_hbm_peak": round((bc + bd) * n * T * K / elapsed / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes_per_elem": bc + bd},
         "other_launch_granularities": other_modes,
         "bf16_state": bf16_state,
         "compression_ratio_vs_bf16": round(2 / (bits / 8 + 4 / group), 3),
