@@ -4,7 +4,8 @@
  * no Python and no torch.  Each step's codes, scales, sender state, receiver
  * base and bf16 output are copied back and compared byte for byte with the CPU
  * oracle (oracle/libcfz_oracle.so, test infrastructure) run on the same inputs;
- * cfz_lowrank's reconstruction is compared with the oracle's fp64 one.  Prints
+ * cfz_lowrank's reconstruction is compared with the oracle's fp64 one, and the
+ * deferred low-rank error-feedback sender with the plain one.  Prints
  * one line per case before its GPU work, and "OK" at the end.
  */
 #include <hip/hip_runtime_api.h>
@@ -272,6 +273,121 @@ static int run_lowrank(void)
     return 0;
 }
 
+/* The rank-r compressor inside error feedback from C: a plain sender
+ * (cfz_lowrank_ef_compress) and a deferred one (cfz_lowrank_ef_compress_deferred,
+ * then cfz_lowrank_ef_flush) on the same inputs, each with its receiver, the
+ * previous step's V as Q0 from the second step on.  After every step the factors,
+ * prev and the receivers' base and bf16 output agree bit for bit; after the flush
+ * so does err. */
+static int run_lowrank_ef(void)
+{
+    enum { B = 2, M = 64, NN = 128, R = 8, T = 2, S = 4, E = B * M * NN };
+    printf("case lowrank-ef batch=%d m=%d n=%d r=%d T=%d steps=%d, plain and deferred\n", B, M, NN,
+           R, T, S);
+    fflush(stdout);
+    static uint16_t x[(S + 1) * E];
+    static float Q0[B * NN * R];
+    uint32_t seed = 91u;
+    float drift[M * R], dir[NN * R];
+    for (int i = 0; i < M * R; ++i)
+        drift[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+    for (int t = 0; t <= S; ++t) {
+        for (int i = 0; i < NN * R; ++i)
+            dir[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+        for (int b = 0; b < B; ++b)
+            for (int i = 0; i < M; ++i)
+                for (int j = 0; j < NN; ++j) {
+                    float a = 0.05f * ((float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f);
+                    for (int k = 0; k < R; ++k)
+                        a += 0.1f * (float)t * drift[i * R + k] * dir[j * R + k];
+                    x[(size_t)t * E + (b * M + i) * NN + j] = to_bf16(a + (float)(b + 1));
+                }
+    }
+    for (int i = 0; i < B * NN * R; ++i)
+        Q0[i] = (float)(lcg(&seed) >> 8) / 16777216.0f - 0.5f;
+
+    const size_t ws_bytes = cfz_lowrank_ef_workspace_bytes(B, M, NN, R);
+    if (ws_bytes == 0)
+        FAIL("workspace size");
+    /* [0]: plain sender and its receiver, [1]: deferred */
+    void *dx, *dQ0, *prev[2], *err[2], *U[2], *V[2], *RU[2], *ws[2], *base[2], *xhat[2];
+    HIP(hipMalloc(&dx, sizeof x));
+    HIP(hipMalloc(&dQ0, sizeof Q0));
+    HIP(hipMemcpy(dx, x, sizeof x, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(dQ0, Q0, sizeof Q0, hipMemcpyHostToDevice));
+    for (int k = 0; k < 2; ++k) {
+        HIP(hipMalloc(&prev[k], 2 * E));
+        HIP(hipMalloc(&err[k], 4 * E));
+        HIP(hipMalloc(&U[k], 4 * B * M * R));
+        HIP(hipMalloc(&V[k], 4 * B * NN * R));
+        HIP(hipMalloc(&RU[k], 4 * B * R * R));
+        HIP(hipMalloc(&ws[k], ws_bytes));
+        HIP(hipMalloc(&base[k], 4 * E));
+        HIP(hipMalloc(&xhat[k], 2 * E));
+        CFZ(cfz_lowrank_ef_warmup(E, (const uint16_t *)dx, (uint16_t *)prev[k], (float *)err[k],
+                                  (float *)base[k], NULL));
+    }
+    if (cfz_lowrank_ef_compress_deferred(B, M, NN, R, T, 2, (const uint16_t *)dx,
+                                         (uint16_t *)prev[1], (float *)err[1],
+                                         (const float *)dQ0, (float *)U[1], (float *)V[1],
+                                         (float *)RU[1], ws[1], ws_bytes, NULL) != CFZ_ERR_SHAPE)
+        FAIL("pending = 2 must be refused");
+    if (cfz_lowrank_ef_flush(B, M, NN, R, (const float *)U[1], (const float *)V[1],
+                             (const float *)RU[1], NULL, NULL) != CFZ_ERR_NULL)
+        FAIL("a flush without err must be refused");
+    static unsigned char h0[4 * E], h1[4 * E];
+    for (int t = 1; t <= S; ++t) {
+        const uint16_t *xt = (const uint16_t *)dx + (size_t)t * E;
+        for (int k = 0; k < 2; ++k) {
+            const float *q0 = t == 1 ? (const float *)dQ0 : (const float *)V[k];
+            if (k == 0)
+                CFZ(cfz_lowrank_ef_compress(B, M, NN, R, T, xt, (uint16_t *)prev[k],
+                                            (float *)err[k], q0, (float *)U[k], (float *)V[k],
+                                            (float *)RU[k], ws[k], ws_bytes, NULL));
+            else
+                CFZ(cfz_lowrank_ef_compress_deferred(B, M, NN, R, T, t > 1, xt,
+                                                     (uint16_t *)prev[k], (float *)err[k], q0,
+                                                     (float *)U[k], (float *)V[k], (float *)RU[k],
+                                                     ws[k], ws_bytes, NULL));
+            CFZ(cfz_lowrank_ef_decompress(B, M, NN, R, (const float *)U[k], (const float *)V[k],
+                                          (const float *)RU[k], (float *)base[k],
+                                          (uint16_t *)xhat[k], NULL));
+        }
+        HIP(hipDeviceSynchronize());
+        const struct { void **p; size_t bytes; const char *name; } cmp[] = {
+            {U, 4 * B * M * R, "U"}, {V, 4 * B * NN * R, "V"}, {RU, 4 * B * R * R, "RU"},
+            {prev, 2 * E, "prev"}, {base, 4 * E, "base"}, {xhat, 2 * E, "xhat"}};
+        for (size_t c = 0; c < sizeof cmp / sizeof cmp[0]; ++c) {
+            HIP(hipMemcpy(h0, cmp[c].p[0], cmp[c].bytes, hipMemcpyDeviceToHost));
+            HIP(hipMemcpy(h1, cmp[c].p[1], cmp[c].bytes, hipMemcpyDeviceToHost));
+            if (memcmp(h0, h1, cmp[c].bytes) != 0)
+                FAIL("step %d: %s of the deferred sender differs from the plain one", t,
+                     cmp[c].name);
+        }
+    }
+    CFZ(cfz_lowrank_ef_flush(B, M, NN, R, (const float *)U[1], (const float *)V[1],
+                             (const float *)RU[1], (float *)err[1], NULL));
+    HIP(hipDeviceSynchronize());
+    HIP(hipMemcpy(h0, err[0], 4 * E, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(h1, err[1], 4 * E, hipMemcpyDeviceToHost));
+    if (memcmp(h0, h1, 4 * E) != 0)
+        FAIL("err after the flush differs from the plain sender's");
+    printf("  %d steps bit-identical, err after the flush too\n", S);
+    for (int k = 0; k < 2; ++k) {
+        HIP(hipFree(prev[k]));
+        HIP(hipFree(err[k]));
+        HIP(hipFree(U[k]));
+        HIP(hipFree(V[k]));
+        HIP(hipFree(RU[k]));
+        HIP(hipFree(ws[k]));
+        HIP(hipFree(base[k]));
+        HIP(hipFree(xhat[k]));
+    }
+    HIP(hipFree(dx));
+    HIP(hipFree(dQ0));
+    return 0;
+}
+
 int main(void)
 {
     static uint16_t x[(STEPS + 1) * N];
@@ -288,6 +404,8 @@ int main(void)
         if (run_case(cases[i][0], cases[i][1], cases[i][2], cases[i][3], x))
             return 1;
     if (run_lowrank())
+        return 1;
+    if (run_lowrank_ef())
         return 1;
     printf("OK\n");
     return 0;

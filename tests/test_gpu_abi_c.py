@@ -3,7 +3,8 @@ device memory with the HIP runtime API, calls libcfz only through include/cfz.h
 (no Python, no torch) and compares every step's codes, scales, states and bf16
 output byte for byte with the C oracle, over int4/int2, group sizes 32-128, the
 three error-feedback modes and fp32/bf16 state; then cfz_lowrank from C, its
-reconstruction within 1e-3 of the oracle's."""
+reconstruction within 1e-3 of the oracle's; then the low-rank error-feedback loop
+with the plain and the deferred sender, bit-identical step by step."""
 import os
 import shutil
 import subprocess
