@@ -259,6 +259,7 @@ def test_graph_replay_matches_eager_every_replay():
 @pytest.mark.parametrize("batch,m,n,r,T,warm", [(2, 130, 264, 16, 2, False),
                                                 (1, 1100, 264, 32, 1, True),
                                                 (3, 96, 136, 5, 2, True),
+                                                (2, 100, 136, 12, 0, False),
                                                 (57, 1024, 3072, 16, 2, True)])
 def test_deferred_sender_matches_plain_bit_for_bit(batch, m, n, r, T, warm):
     """The deferred sender (each step's update applied inside the next step's residual pass)
