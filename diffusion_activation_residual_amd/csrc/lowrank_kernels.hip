@@ -11,7 +11,9 @@
 // product carries about 16 bits of the skinny operand instead of 8.  For
 // r <= 16 and n <= 3072, Y = A Q and Z = A^T Y run as one pass over A
 // (lr_ata_kernel, lr_ata8_kernel for r <= 8); otherwise as two (lr_aq_kernel,
-// lr_aty_kernel).
+// lr_aty_kernel).  With T >= 1 the sample Q0 enters the first product as it is
+// (see run_lowrank); at r <= 8 the first one-pass product also splits it into
+// its hi / lo operands itself.
 //
 // orth() is Cholesky-QR: Gram matrix G = M^T M accumulated in fp64 from fp32
 // rows, r x r Cholesky and triangular inverse in fp64, then M R^-1 row by row.
@@ -21,8 +23,9 @@
 // exceeds 2^14.5 (kappa^2 u_fp64 > u_fp32).  For r <= 16 this is two launches
 // (Gram partials, then factorisations and apply in lr_cholapply_kernel; for P
 // the final A Q leaves the Gram partials, so one); for r > 16 five, the second
-// pass's two leaving at once for the matrices that do not need it.  A pivot <= 1e-13 * trace(G) / r (or not finite) drops the
-// column: zero Q column, zero R row and column.
+// pass's two leaving at once for the matrices that do not need it.  A pivot
+// <= 1e-13 * trace(G) / r (or not finite) drops the column: zero Q column, zero
+// R row and column.
 //
 // Skinny operands live in the workspace in "operand layout": hi and lo bf16
 // planes of shape [L/8][RP][8], where RP = 16 or 32 is r padded to the MFMA
